@@ -1,0 +1,291 @@
+"""The five decode workloads, seeded, plus reduced variants for fast parity runs.
+
+Every workload is a description of one or more decode steps over a block
+pool.  Context lengths count the token written in that step (the new token
+goes to position ``length - 1`` and the step's query attends over all
+``length`` positions).  Pools are numpy arrays ``[N][2][Hkv][B][D]`` holding
+float32 values, or bf16 bit patterns as uint16.  Blocks that hold no token of
+any sequence are filled with NaN so that a kernel reading outside a
+sequence's blocks cannot go unnoticed.
+
+Seeds: workload ``k`` draws from ``numpy.random.default_rng(k)`` (reduced
+variants from ``default_rng(100 + k)``), in this order: lengths, block
+placement, resident K/V contents, then per step the query and the new
+tokens' K and V.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CONFIG_NAMES = {
+    1: "worked example: lengths 25/47/12, B16, 16-block pool, 4/4 heads, D64, fp32",
+    2: "Qwen3-8B layer, batch 64, context 4,100-4,164, B16, bf16, 38,348-block pool",
+    3: "Qwen3-8B layer, batch 128, context 12-2,048, 512-token prefix shared by groups of 4, B16, bf16",
+    4: "70B-shaped layer, batch 8 x 32,768, 64/8 heads, B32, bf16, 8,192-block pool",
+    5: "Qwen3-8B layer, 512 lognormal contexts (median 600), 32 decode steps, B16, bf16, 38,348-block pool",
+}
+
+_BF16_NAN = np.uint16(0x7FC0)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bit patterns.
+
+    Inputs must be finite.  Adding 0x7FFF plus the lowest kept bit and
+    truncating the low 16 bits is round-to-nearest-even on the bit pattern.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _blocks_for(num_tokens: int, block_size: int) -> int:
+    # table rows are sized to hold the tokens (rounded up to whole blocks)
+    return (int(num_tokens) + block_size - 1) // block_size
+
+
+@dataclass
+class Step:
+    """One decode step: copy-on-write copies, the cache write, then decode."""
+
+    context_lens: np.ndarray  # int32 [S], after this step's write
+    q: np.ndarray  # [S][Hq][D] storage dtype
+    k_new: np.ndarray  # [T][Hkv][D] storage dtype, T = len(write_seq)
+    v_new: np.ndarray
+    write_seq: np.ndarray  # int32 [T]: sequence of each written token
+    write_pos: np.ndarray  # int32 [T]: its position
+    cow_src: np.ndarray  # int32 [P]: shared blocks copied before the write
+    cow_dst: np.ndarray  # int32 [P]: the fresh blocks they are copied to
+    new_blocks: list = field(default_factory=list)  # (seq, logical index, block) taken this step
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str  # "f32" | "bf16"
+    num_blocks: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: np.float32
+    pool: np.ndarray  # state before the first step
+    block_tables: np.ndarray  # int32 [S][max_blocks]; entries past a sequence's blocks are the pad id
+    steps: list
+    null_block: int | None = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.block_tables.shape[0])
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def kv_bytes(self, step: int = 0) -> int:
+        """K and V bytes of the live context tokens read by one decode of ``step``."""
+        lens = self.steps[step].context_lens.astype(np.int64)
+        return int(lens.sum()) * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+
+
+def _empty_pool(num_blocks, num_kv_heads, block_size, head_dim, dtype):
+    shape = (num_blocks, 2, num_kv_heads, block_size, head_dim)
+    if dtype == "bf16":
+        return np.full(shape, _BF16_NAN, dtype=np.uint16)
+    return np.full(shape, np.nan, dtype=np.float32)
+
+
+def _fill_blocks(pool, blocks, rng, dtype, chunk=256):
+    blocks = np.asarray(sorted(set(int(b) for b in blocks)), dtype=np.int64)
+    per_block = pool.shape[1:]
+    for i in range(0, len(blocks), chunk):
+        sel = blocks[i:i + chunk]
+        pool[sel] = _normal(rng, (len(sel),) + per_block, dtype)
+
+
+def _tables_array(rows, pad):
+    width = max(1, max(len(r) for r in rows))
+    out = np.full((len(rows), width), pad, dtype=np.int32)
+    for s, r in enumerate(rows):
+        out[s, :len(r)] = r
+    return out
+
+
+def _decode_step(rng, lens, num_q_heads, num_kv_heads, head_dim, dtype, cow_src=(), cow_dst=(), new_blocks=()):
+    S = len(lens)
+    q = _normal(rng, (S, num_q_heads, head_dim), dtype)
+    k_new = _normal(rng, (S, num_kv_heads, head_dim), dtype)
+    v_new = _normal(rng, (S, num_kv_heads, head_dim), dtype)
+    return Step(
+        context_lens=np.asarray(lens, dtype=np.int32),
+        q=q, k_new=k_new, v_new=v_new,
+        write_seq=np.arange(S, dtype=np.int32),
+        write_pos=(np.asarray(lens, dtype=np.int32) - 1),
+        cow_src=np.asarray(cow_src, dtype=np.int32), cow_dst=np.asarray(cow_dst, dtype=np.int32),
+        new_blocks=list(new_blocks),
+    )
+
+
+def make_custom(*, name, seed, dtype, num_blocks, num_q_heads, num_kv_heads, head_dim, block_size,
+                lengths, placement="free_list", prefix_tokens=0, group=4, num_steps=1):
+    """General builder behind every workload.
+
+    ``placement``: ``"free_list"`` keeps block 0 as the null block and pops
+    the other blocks from a seeded shuffle of the free list; ``"permutation"``
+    uses a seeded permutation of the whole pool.  ``prefix_tokens > 0``
+    makes each run of ``group`` consecutive sequences share the blocks of a
+    common prefix of that many tokens; a sequence whose write lands in a
+    shared block gets a fresh block and a copy first when others still hold
+    it, and writes in place when it is the last holder.  ``num_steps > 1``
+    grows every sequence by one token per step, taking a fresh block from the
+    free list when a write starts a new block.
+    """
+    rng = np.random.default_rng(seed)
+    B = block_size
+    lengths = np.asarray(lengths, dtype=np.int64)
+    S = len(lengths)
+    if placement == "free_list":
+        free = list(rng.permutation(np.arange(1, num_blocks)))
+        null_block, pad = 0, 0
+    elif placement == "permutation":
+        free = list(rng.permutation(np.arange(num_blocks)))
+        null_block, pad = None, 0
+    else:
+        raise ValueError(placement)
+    free.reverse()  # pop() from the end == take the front of the shuffled queue
+
+    def take():
+        if not free:
+            raise RuntimeError(f"{name}: pool of {num_blocks} blocks exhausted")
+        return int(free.pop())
+
+    rows = [[] for _ in range(S)]
+    resident = set()  # blocks whose contents are drawn now
+    cow_src, cow_dst = [], []
+    if prefix_tokens:
+        prefix_blocks = prefix_tokens // B
+        assert prefix_blocks * B == prefix_tokens, "the shared prefix must be whole blocks"
+        for g0 in range(0, S, group):
+            members = list(range(g0, min(S, g0 + group)))
+            n_need = [_blocks_for(lengths[s], B) for s in members]
+            shared = [take() for _ in range(min(prefix_blocks, max(n_need)))]
+            resident.update(shared)
+            holders = {b: 0 for b in shared}
+            for s, n in zip(members, n_need):
+                for j in range(n):
+                    if j < prefix_blocks:
+                        rows[s].append(shared[j])
+                        holders[shared[j]] += 1
+                    else:
+                        b = take()
+                        rows[s].append(b)
+                        resident.add(b)
+            for s in members:
+                j = int(lengths[s] - 1) // B
+                if j < prefix_blocks:
+                    b = rows[s][j]
+                    if holders[b] > 1:
+                        fresh = take()
+                        holders[b] -= 1
+                        rows[s][j] = fresh
+                        cow_src.append(b)
+                        cow_dst.append(fresh)
+    else:
+        for s in range(S):
+            rows[s] = [take() for _ in range(_blocks_for(lengths[s], B))]
+            resident.update(rows[s])
+
+    # blocks the later steps take, in step order then sequence order
+    growth = [[] for _ in range(num_steps)]
+    for k in range(1, num_steps):
+        for s in range(S):
+            pos = int(lengths[s]) + k - 1
+            if pos % B == 0:
+                b = take()
+                growth[k].append((s, len(rows[s]), b))
+                rows[s].append(b)
+
+    tables = _tables_array(rows, pad)
+    pool = _empty_pool(num_blocks, num_kv_heads, B, head_dim, dtype)
+    _fill_blocks(pool, resident, rng, dtype)
+
+    steps = []
+    for k in range(num_steps):
+        steps.append(_decode_step(rng, lengths + k, num_q_heads, num_kv_heads, head_dim, dtype,
+                                  cow_src if k == 0 else (), cow_dst if k == 0 else (), growth[k]))
+    scale = np.float32(1.0) / np.sqrt(np.float32(head_dim))
+    return Workload(name=name, dtype=dtype, num_blocks=num_blocks, num_q_heads=num_q_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, scale=np.float32(scale),
+                    pool=pool, block_tables=tables, steps=steps, null_block=null_block,
+                    meta={"prefix_tokens": prefix_tokens, "group": group, "placement": placement})
+
+
+def _lognormal_lengths(rng, n, median, sigma, lo, hi):
+    return np.clip(np.rint(rng.lognormal(mean=np.log(median), sigma=sigma, size=n)), lo, hi).astype(np.int64)
+
+
+def make_config(k: int, small: bool = False) -> Workload:
+    """Workload ``k`` (1-5).  ``small=True`` keeps its shapes and structure at sizes
+    the oracle checks in seconds (several tiles, a ragged tail)."""
+    seed = (100 + k) if small else k
+    if k == 1:
+        return make_custom(name="cfg1-worked", seed=seed, dtype="f32", num_blocks=16, num_q_heads=4,
+                           num_kv_heads=4, head_dim=64, block_size=16, lengths=[25, 47, 12],
+                           placement="permutation")
+    if k == 2:
+        rng = np.random.default_rng(seed)
+        if small:
+            lens = rng.integers(100, 165, size=6)
+            n = 1024
+        else:
+            lens = rng.integers(4100, 4165, size=64)
+            n = 38348
+        return make_custom(name="cfg2-qwen3-8b-b64" + ("-small" if small else ""), seed=seed + 1000,
+                           dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, lengths=lens)
+    if k == 3:
+        rng = np.random.default_rng(seed)
+        if small:
+            lens = rng.integers(12, 300, size=12)
+            n, prefix = 1024, 128
+        else:
+            lens = rng.integers(12, 2049, size=128)
+            n, prefix = 38348, 512
+        return make_custom(name="cfg3-mixed-prefix" + ("-small" if small else ""), seed=seed + 1000,
+                           dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, lengths=lens, prefix_tokens=prefix, group=4)
+    if k == 4:
+        if small:
+            S, L, n = 2, 2048, 128
+        else:
+            S, L, n = 8, 32768, 8192
+        return make_custom(name="cfg4-70b-long" + ("-small" if small else ""), seed=seed, dtype="bf16",
+                           num_blocks=n, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+                           lengths=[L] * S, placement="permutation")
+    if k == 5:
+        if small:
+            S, median, hi, n, steps = 24, 60, 2048, 1024, 4
+        else:
+            S, median, hi, n, steps = 512, 600, 40960, 38348, 32
+        s = seed
+        while True:
+            rng = np.random.default_rng(s)
+            lens = _lognormal_lengths(rng, S, median, 1.0, 1, hi)
+            need = sum(_blocks_for(L + steps - 1, 16) for L in lens)
+            if need <= n - 1:
+                break
+            s += 1
+        return make_custom(name="cfg5-high-concurrency" + ("-small" if small else ""), seed=s + 1000,
+                           dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, lengths=lens, num_steps=steps)
+    raise ValueError(f"no workload {k}")
