@@ -1,0 +1,222 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: slot mapping, cache
+write of the step's new tokens, then paged decode attention (copy-on-write
+block copies too when the workload has them).  Inputs are seeded synthetic
+data already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--partition-size 0]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "decode attention KV-read GB/s (and % HBM peak); sequences·layers/sec"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1-5 (default: 2, the Qwen3-8B batch-64 layer)")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--decode-reps", type=int, default=50, help="timed decode-only launches for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the oracle's timed sample")
+    ap.add_argument("--skip-check", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_121_amd", "csrc", "decode.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: int, partition_size: int):
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current decode kernel source at this partition size; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    e = t.get(f"workload{workload}")
+    if not e or e.get("decode_source_sha256_16") != kernel_source_digest() or e.get("partition_size") != partition_size:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_seqs: int):
+    """The float64 oracle on a bounded sample of the same workload, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    st = w.steps[0]
+    sel = list(range(min(n_seqs, w.num_seqs)))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        paged.decode_ref(w.pool, st.q[sel], w.block_tables[sel], st.context_lens[sel], float(w.scale))
+        dt = time.perf_counter() - t0
+    kv = int(st.context_lens[sel].astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle decode of sequences 0-{len(sel) - 1} (all {w.num_q_heads} query heads) "
+                      f"of the same workload: {kv / 1e9:.3f} GB of KV in {dt:.1f} s, one thread",
+            "seq_layers_per_s": len(sel) / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by sequence or KV head with no exchange step); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    from workloads import CONFIG_NAMES, make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    w = make_config(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    st = w.steps[0]
+    print(f"[bench] workload {args.workload}: {w.name} generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def dev_data(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    pool = pa.PagedKVPool(dev_data(w.pool))
+    tables = dev_i32(w.block_tables)
+    lens = dev_i32(st.context_lens)
+    q = dev_data(st.q)
+    k_new, v_new = dev_data(st.k_new), dev_data(st.v_new)
+    wseq, wpos = dev_i32(st.write_seq), dev_i32(st.write_pos)
+    cow_src, cow_dst = dev_i32(st.cow_src), dev_i32(st.cow_dst)
+    max_len = int(st.context_lens.max())
+    part = args.partition_size or pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads, max_len)
+    nbytes = pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, max_len, part)
+    workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    counters = torch.zeros(w.num_seqs * w.num_kv_heads, dtype=torch.int32, device=dev)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    slots = torch.empty(len(st.write_seq), dtype=torch.int64, device=dev)
+    scale = float(w.scale)
+    torch.cuda.synchronize()
+
+    def decode():
+        pa.pa_decode(pool, q, tables, lens, scale=scale, max_context_len=max_len, partition_size=part,
+                     out=out, workspace=workspace, counters=counters)
+
+    def step():
+        if len(st.cow_src):
+            pa.pa_block_copy(pool, cow_src, cow_dst)
+        pa.pa_slot_mapping(pool, tables, wseq, wpos, out=slots)
+        pa.pa_cache_write(pool, k_new, v_new, slots)
+        decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # decode-only launches, each bracketed by events on the stream it runs on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.decode_reps)]
+    for a, b in ev:
+        a.record(stream)
+        decode()
+        b.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec_avg_ms = float(dec_ms.mean())
+
+    kv_bytes = w.kv_bytes(0)
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+
+    check = None
+    if not args.skip_check:
+        from oracle import paged
+        got = out.cpu().numpy()
+        s_max = int(np.argmax(st.context_lens))
+        small_rows = [int(b) for b in w.block_tables[s_max, :-(-max_len // w.block_size)]]
+        cow = dict(zip(st.cow_dst.tolist(), st.cow_src.tolist()))  # this step's copy-on-write sources
+        small = np.stack([w.pool[cow.get(b, b)] for b in small_rows])
+        tbl = np.arange(len(small_rows), dtype=np.int32)[None, :]
+        slot = paged.slot_mapping_ref(tbl, [0], [int(st.write_pos[s_max])], w.block_size)
+        small = paged.cache_write_ref(small, st.k_new[s_max:s_max + 1], st.v_new[s_max:s_max + 1], slot)
+        want = paged.decode_one_ref(small, st.q[s_max:s_max + 1], tbl, [int(st.context_lens[s_max])], scale, 0, 0)
+        check = float(np.abs(got[s_max, 0] - want).max())
+        if not (check <= 2e-3 and np.isfinite(got).all()):
+            print(f"[bench] PARITY FAILURE: max abs err {check}", file=sys.stderr)
+            sys.exit(1)
+
+    traffic = measured_traffic(args.workload, part)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seqs)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 K/V and Q, fp32 accumulate", "f32": "f32"}[w.dtype],
+        "data": "synthetic (seeded N(0,1) K/V/Q; lengths, placement and sharing per the workload recipe)",
+        "config": {
+            "workload": f"workload {args.workload}: {CONFIG_NAMES[args.workload]}",
+            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": w.num_blocks,
+            "context_tokens": int(st.context_lens.sum()), "max_context_len": max_len,
+            "partition_size": part, "kv_bytes_per_step": kv_bytes,
+        },
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_gbs": round(achieved, 1),
+        "seq_layers_per_s": round(w.num_seqs / (dec_avg_ms * 1e-3), 1),
+        "step_seq_layers_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel", "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": cpu,
+        "sampled_max_abs_err": check,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache decode path.
+ *
+ * The operations follow the pages this library was built from:
+ *   [AINEW] "PagedAttention: KV-cache virtual memory technique improves
+ *           inference efficiency" (news.ainew.jp; the title is Japanese on
+ *           the page)
+ *   [SALIV] "How PagedAttention Eliminates KV-Cache Fragmentation"
+ *   [VIBE]  "PagedAttention, explained." (vibeengines.com)
+ *   [HRL]   "What Does PagedAttention Actually Optimize?" (hrletsgo.me)
+ *   [TSS]   "Paged Attention: Virtual Memory for the KV Cache"
+ *           (theservingstack.com)
+ *
+ * General contract (every entry point):
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise;
+ *     the pa_pool descriptor itself is a host struct read during the call.
+ *   - A call validates its scalar arguments on the host, enqueues its
+ *     kernels on `stream` and returns; it never synchronises the stream.
+ *   - The caller owns all memory.  The library allocates nothing and keeps
+ *     no pointer after the call returns.
+ *   - Scalar errors return a negative pa_status and enqueue nothing.  A
+ *     failed launch returns PA_ERR_HIP.  A call with zero work returns PA_OK
+ *     and enqueues nothing.
+ *   - Device contents are the caller's contract.  Kernels never access
+ *     memory outside the buffers described here, whatever those contents
+ *     are: an out-of-range id or slot is skipped (writes, copies, slot
+ *     mapping) or turns the affected outputs into NaN (decode), as each
+ *     entry point states.
+ *   - Calls that overlap on one stream run in order; calls on different
+ *     streams that touch the same pool region race.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes */
+  PA_ERR_UNSUPPORTED = -2, /* a shape or dtype this build has no kernel for   */
+  PA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small           */
+  PA_ERR_HIP = -4          /* the HIP runtime rejected a launch               */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * The physical block pool ([AINEW] "PagedAttention in one picture";
+ * [TSS] "Paging": fixed-size blocks carved out of the cache memory).
+ * `base` points at num_blocks * 2 * num_kv_heads * block_size * head_dim
+ * elements laid out as [num_blocks][2][num_kv_heads][block_size][head_dim]:
+ * index 0 of the second axis holds K and index 1 holds V, so one physical
+ * block is one contiguous chunk and each (block, head) K or V tile is
+ * contiguous.  Supported: block_size 16 or 32, head_dim 64 or 128, dtype
+ * PA_F32 or PA_BF16 (bf16 = upper half of an IEEE binary32).
+ */
+typedef struct {
+  void *base;
+  int64_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_pool;
+
+/*
+ * Slot of each token written this step ([TSS] "Finding a token: position,
+ * block, slot": the slot is the physical block times the block size plus the
+ * offset inside the block; [HRL] section 5 for the table lookup).
+ *   block_tables : int32 [num_seqs][max_blocks_per_seq], physical block ids.
+ *   seq_ids      : int32 [num_tokens], the sequence of each token.
+ *   positions    : int32 [num_tokens], its position inside that sequence.
+ *   slot_mapping : int64 [num_tokens], output.
+ * slot = block_tables[seq][pos / block_size] * block_size + pos % block_size.
+ * A token whose seq id lies outside [0, num_seqs), whose position is
+ * negative or beyond the table row, or whose table entry lies outside
+ * [0, num_blocks) gets slot -1 (which pa_cache_write skips).
+ */
+int pa_slot_mapping(const pa_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    int32_t num_seqs, const int32_t *seq_ids, const int32_t *positions,
+                    int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/*
+ * Scatter each new token's K and V into its slot ([VIBE] vLLM procedure
+ * step 4; [HRL] section 17 `write_kv`; the fused write kernel named in
+ * [VIBE] "Across GPUs").
+ *   k_new, v_new : [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *   slot_mapping : int64 [num_tokens].
+ * pool[slot / B][0][h][slot % B][:] = k_new[i][h][:] and likewise V at index
+ * 1, for every head, copied bit for bit.  Negative slots and slots at or
+ * beyond num_blocks * block_size are skipped.  Two tokens with the same slot
+ * in one call is a caller error (which one lands is unspecified).
+ */
+int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new,
+                   const int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/*
+ * Whole-block copies for copy-on-write ([AINEW] copy-on-write passage;
+ * [SALIV] "Advanced Memory Sharing and Copy-on-Write"; [VIBE] step 6 and
+ * the block-copy kernel named in "Across GPUs").
+ *   src_blocks, dst_blocks : int32 [num_pairs].
+ * pool[dst[j]] = pool[src[j]] for every pair: K and V, every head, every
+ * slot.  A pair with an id outside [0, num_blocks) is skipped.  Destinations
+ * must be distinct and must not appear among the sources (else the result
+ * is unspecified).
+ */
+int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks,
+                  int32_t num_pairs, hipStream_t stream);
+
+/*
+ * Partition size (tokens) pa_decode uses when passed partition_size == 0.
+ * Returns a positive multiple of the block size, or a negative pa_status.
+ */
+int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len);
+
+/*
+ * Device workspace bytes pa_decode needs for these arguments (0 when every
+ * sequence fits one partition).  Returns 0 for invalid arguments too; the
+ * decode call itself reports those.
+ */
+size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * One decode step of paged attention ([VIBE] step 5: the kernel fetches key
+ * and value blocks through the table, block by block; [HRL] section 8: the
+ * result is ordinary softmax(q K^T * scale) V; [HRL] section 14: per token,
+ * logical block, physical block, offset, read).
+ *   q            : [num_seqs][num_q_heads][head_dim], pool dtype.
+ *   out          : float32 [num_seqs][num_q_heads][head_dim], output.
+ *   block_tables : int32 [num_seqs][max_blocks_per_seq].
+ *   context_lens : int32 [num_seqs], tokens each query attends over (the
+ *                  token written this step included).
+ *   scale        : multiplier of q.k (usually 1/sqrt(head_dim)).
+ *   max_context_len : host-known upper bound of context_lens.
+ *   partition_size  : tokens per split-context partition; 0 = automatic;
+ *                  else a positive multiple of block_size, at most 512
+ *                  blocks.
+ *   workspace    : scratch for split-context partial results, at least
+ *                  pa_decode_workspace_size() bytes, 256-byte aligned (may
+ *                  be NULL when that size is 0).  Contents need no
+ *                  initialisation.
+ *   counters     : uint32 [num_seqs][num_kv_heads] arrival counters of the
+ *                  split-context combine (may be NULL when the workspace
+ *                  size is 0).  They must be zero before the first call;
+ *                  every call leaves them zero again, so one zeroed buffer
+ *                  large enough for the biggest batch can be reused.
+ * Calls sharing a workspace or counters must not overlap in time (calls on
+ * one stream never do).  Query head hq reads KV head
+ * hq / (num_q_heads / num_kv_heads); the group size must be 1, 2, 4 or 8.
+ * Output rows of a sequence with a context length of 0 are zero; rows of a
+ * sequence whose context length is negative, exceeds max_context_len or its
+ * table row, or whose table holds an id outside [0, num_blocks) among its
+ * first ceil(len / block_size) entries, are NaN.
+ */
+int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+              int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
+              void *workspace, size_t workspace_bytes, uint32_t *counters, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *pa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,304 @@
+"""Python binding of libpa.so, the MI355X paged KV-cache decode library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in ``include/pa.h``.  Functions carry the C names:
+
+* ``pa_slot_mapping(pool, block_tables, seq_ids, positions) -> slots``
+* ``pa_cache_write(pool, k_new, v_new, slot_mapping)``
+* ``pa_block_copy(pool, src_blocks, dst_blocks)``
+* ``pa_decode(pool, q, block_tables, context_lens, ...) -> out``
+* ``pa_decode_workspace_size(...)``, ``pa_decode_partition_size(...)``
+
+Tensors live on a ROCm device (torch provides memory and the current
+stream).  There is no fallback: if libpa.so is missing or the device is not
+a GPU, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "PaError",
+    "PagedKVPool",
+    "decode_counters",
+    "library_path",
+    "load_library",
+    "pa_block_copy",
+    "pa_cache_write",
+    "pa_decode",
+    "pa_decode_partition_size",
+    "pa_decode_workspace_size",
+    "pa_slot_mapping",
+    "pa_status_str",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+PA_F32, PA_BF16 = 0, 1
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libpa.so")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pa_status_str(status)} (status {status})")
+
+
+class pa_pool(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_VP, _I32, _I64, _SZ, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_POOLP = ctypes.POINTER(pa_pool)
+_SIGNATURES = {
+    "pa_slot_mapping": (_I32, [_POOLP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "pa_cache_write": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP]),
+    "pa_block_copy": (_I32, [_POOLP, _VP, _VP, _I32, _VP]),
+    "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
+    "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
+    "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _VP, _SZ, _VP, _VP]),
+    "pa_status_str": (ctypes.c_char_p, [_I32]),
+}
+
+
+def load_library(path: str | None = None):
+    """Load libpa.so (once) and declare its C signatures.  Raises if it is missing."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or library_path()
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is not built; run `python -m paged_kv_cache_121_amd.build` "
+                "(hipcc, gfx950) before using the paged decode path")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def pa_status_str(status: int) -> str:
+    return load_library().pa_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PaError(status, where)
+
+
+def _stream(t) -> ctypes.c_void_p:
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t, name: str, dtype=None, ndim=None, device=None):
+    torch = _torch()
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must live on a ROCm device (no CPU path exists)")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None:
+        _need(t.dim() == ndim, f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if device is not None:
+        _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+class PagedKVPool:
+    """A physical block pool: torch tensor ``[num_blocks][2][num_kv_heads][block_size][head_dim]``.
+
+    Index 0 of the second axis is K, index 1 is V.  float32 or bfloat16.
+    """
+
+    def __init__(self, data):
+        torch = _torch()
+        _dev_tensor(data, "pool", ndim=5)
+        _need(data.shape[1] == 2, "pool axis 1 must be 2 (K, V)")
+        _need(data.dtype in (torch.float32, torch.bfloat16), "pool dtype must be float32 or bfloat16")
+        self.data = data
+        self.num_blocks, _, self.num_kv_heads, self.block_size, self.head_dim = (int(x) for x in data.shape)
+        self.dtype_code = PA_BF16 if data.dtype == torch.bfloat16 else PA_F32
+        self._desc = pa_pool(data.data_ptr(), self.num_blocks, self.num_kv_heads, self.block_size,
+                             self.head_dim, self.dtype_code)
+
+    @classmethod
+    def empty(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype, device="cuda"):
+        torch = _torch()
+        return cls(torch.empty((num_blocks, 2, num_kv_heads, block_size, head_dim), dtype=dtype, device=device))
+
+    @property
+    def device(self):
+        return self.data.device
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+
+def pa_slot_mapping(pool: PagedKVPool, block_tables, seq_ids, positions, out=None):
+    """int64 slot of each (seq_ids[i], positions[i]) token; -1 where out of range."""
+    torch = _torch()
+    dev = pool.device
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2, dev)
+    _dev_tensor(seq_ids, "seq_ids", torch.int32, 1, dev)
+    _dev_tensor(positions, "positions", torch.int32, 1, dev)
+    _need(seq_ids.shape == positions.shape, "seq_ids and positions must have the same length")
+    n = int(positions.shape[0])
+    if out is None:
+        out = torch.empty(n, dtype=torch.int64, device=dev)
+    _dev_tensor(out, "out", torch.int64, 1, dev)
+    _need(out.shape[0] == n, "out must have one slot per token")
+    lib = load_library()
+    _check(lib.pa_slot_mapping(pool.desc, _ptr(block_tables), int(block_tables.shape[1]),
+                               int(block_tables.shape[0]), _ptr(seq_ids), _ptr(positions), _ptr(out), n,
+                               _stream(out)), "pa_slot_mapping")
+    return out
+
+
+def pa_cache_write(pool: PagedKVPool, k_new, v_new, slot_mapping) -> None:
+    """Write each token's K/V ([T][Hkv][D], pool dtype) into its slot (negative: skipped)."""
+    torch = _torch()
+    dev = pool.device
+    shape = None
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, name, pool.data.dtype, 3, dev)
+        _need(tuple(t.shape[1:]) == (pool.num_kv_heads, pool.head_dim), f"{name} must be [T][Hkv][D]")
+        shape = t.shape if shape is None else shape
+        _need(t.shape == shape, "k_new and v_new must have the same shape")
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    _need(slot_mapping.shape[0] == k_new.shape[0], "one slot per token")
+    lib = load_library()
+    _check(lib.pa_cache_write(pool.desc, _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(k_new.shape[0]),
+                              _stream(k_new)), "pa_cache_write")
+
+
+def pa_block_copy(pool: PagedKVPool, src_blocks, dst_blocks) -> None:
+    """pool[dst[j]] = pool[src[j]] for every pair (whole blocks)."""
+    torch = _torch()
+    dev = pool.device
+    _dev_tensor(src_blocks, "src_blocks", torch.int32, 1, dev)
+    _dev_tensor(dst_blocks, "dst_blocks", torch.int32, 1, dev)
+    _need(src_blocks.shape == dst_blocks.shape, "src_blocks and dst_blocks must have the same length")
+    lib = load_library()
+    _check(lib.pa_block_copy(pool.desc, _ptr(src_blocks), _ptr(dst_blocks), int(src_blocks.shape[0]),
+                             _stream(src_blocks)), "pa_block_copy")
+
+
+def pa_decode_partition_size(pool: PagedKVPool, num_seqs: int, num_q_heads: int, max_context_len: int) -> int:
+    r = load_library().pa_decode_partition_size(pool.desc, num_seqs, num_q_heads, max_context_len)
+    _check(min(r, 0), "pa_decode_partition_size")
+    return int(r)
+
+
+def pa_decode_workspace_size(pool: PagedKVPool, num_seqs: int, num_q_heads: int, max_context_len: int,
+                             partition_size: int = 0) -> int:
+    return int(load_library().pa_decode_workspace_size(pool.desc, num_seqs, num_q_heads, max_context_len,
+                                                       partition_size))
+
+
+_workspaces: dict = {}
+_counters: dict = {}
+
+
+def _workspace(device, nbytes: int):
+    """Scratch of at least ``nbytes`` per device, reused across calls (one stream)."""
+    torch = _torch()
+    key = str(device)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+def decode_counters(device, count: int):
+    """Zeroed uint32 arrival counters (as int32) of at least ``count`` entries per device.
+
+    The decode kernels leave them at zero, so they are zeroed only when
+    (re)allocated and can serve every later call on the device's stream.
+    """
+    torch = _torch()
+    key = str(device)
+    buf = _counters.get(key)
+    if buf is None or buf.numel() < count:
+        buf = torch.zeros(max(count, 4096), dtype=torch.int32, device=device)
+        _counters[key] = buf
+    return buf
+
+
+def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | None = None,
+              max_context_len: int | None = None, partition_size: int = 0, out=None, workspace=None,
+              counters=None):
+    """Paged decode attention; returns float32 ``[S][Hq][D]``.
+
+    ``max_context_len`` defaults to the table width times the block size (a
+    bound known without reading ``context_lens`` back from the device).
+    """
+    torch = _torch()
+    dev = pool.device
+    _dev_tensor(q, "q", pool.data.dtype, 3, dev)
+    S, Hq, D = (int(x) for x in q.shape)
+    _need(D == pool.head_dim, "q head_dim must match the pool")
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2, dev)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(block_tables.shape[0] == S and context_lens.shape[0] == S, "one table row and length per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_context_len is None:
+        max_context_len = int(block_tables.shape[1]) * pool.block_size
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _dev_tensor(out, "out", torch.float32, 3, dev)
+    _need(tuple(out.shape) == (S, Hq, D), "out must be [S][Hq][D]")
+    need = pa_decode_workspace_size(pool, S, Hq, max_context_len, partition_size)
+    if workspace is None:
+        ws = _workspace(dev, need) if need else None
+    else:
+        ws = _dev_tensor(workspace, "workspace", torch.uint8, 1, dev)
+    if counters is None:
+        cnt = decode_counters(dev, S * pool.num_kv_heads) if need else None
+    else:
+        cnt = _dev_tensor(counters, "counters", torch.int32, 1, dev)
+        _need(cnt.numel() >= S * pool.num_kv_heads, "counters needs num_seqs * num_kv_heads entries")
+    lib = load_library()
+    _check(lib.pa_decode(pool.desc, _ptr(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
+                         _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size),
+                         _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
+                         _ptr(cnt) if cnt is not None else None, _stream(q)), "pa_decode")
+    return out

@@ -1,0 +1,521 @@
+// Paged decode attention for gfx950 (CDNA4, wave64).
+//
+// What is computed ([HRL] section 8; [VIBE] vLLM procedure step 5): for every
+// sequence s and query head hq, out = softmax(scale * q K^T) V over the
+// sequence's context_lens[s] cached tokens, where token t of the sequence
+// lives in physical block table[s][t / B] at offset t % B.
+//
+// Work decomposition
+//   grid (partition p, KV head h, sequence s); one workgroup of kWaves
+//   wavefronts serves all G = Hq / Hkv query heads of KV head h, so each K/V
+//   byte is read from HBM once per step.  The workgroup owns the blocks
+//   [p * part, (p + 1) * part) of the sequence; wave w takes the workgroup's
+//   blocks w, w + kWaves, ...
+//
+// Lane layout (16 lanes per token)
+//   A (block, head) K or V tile is [B][D] contiguous, so a token's row is
+//   D * elem bytes = 16 lanes x VEC bytes.  Per load step a wavefront reads
+//   64 x VEC contiguous bytes = 4 tokens; lane l holds dims
+//   (l % 16) * EPL ... of token 4 * step + l / 16.  The four 16-lane rows of
+//   the wave are four independent online-softmax streams (each sees every
+//   fourth token) that are merged once at the end of the partition.
+//
+// QK: each lane forms partial dots over its EPL dims for all G heads (bf16:
+//   v_dot2 on packed pairs, exact products with fp32 accumulation), then a
+//   DPP reduce-scatter inside each 16-lane row leaves lane l holding the full
+//   scores of heads sigma(l) ... sigma(l) + HPL - 1.  The query registers are
+//   loaded in a lane-dependent head order (register r holds head r ^ sigma(l))
+//   so every exchange step is uniform across lanes: no selects.
+// Softmax: scores are kept in log2 units (scale * log2 e folded in) and
+//   exponentiated with the hardware exp2.  The running max is raised only
+//   when a score exceeds it by more than kRescaleThreshold, so the rescale
+//   of the accumulators is rare; the normalisation divides it out exactly.
+// PV: each lane accumulates o[head][its EPL dims] for all G heads, taking each
+//   token's probabilities from the lanes of its quad with a DPP broadcast.
+// Masking: tokens at or past the context length get score -inf and value 0
+//   (selected, never multiplied), so poisoned padding cannot leak in.
+// Split context: when a sequence spans more than one partition, every
+//   partition writes (max, sum, unnormalised output) to the workspace and
+//   the last workgroup to arrive (device-scope counter) combines them in
+//   partition order and writes the output, then zeroes the counter.  The
+//   combination order depends only on logical positions, so results are
+//   identical under any physical placement of the blocks.
+
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 16;                    // tokens per pipeline stage
+constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+struct bf16_tag {};
+
+// DPP controls (gfx9 encoding): quad permutations and 16-lane row rotations.
+constexpr int kQuadXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int quad_bcast(int k) { return k * 0x55; }  // [k,k,k,k]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int NW>
+struct Frag {
+  uint32_t w[NW];
+};
+
+template <int NW>
+__device__ __forceinline__ void load_frag(Frag<NW> &f, const char *p) {
+  if constexpr (NW == 2) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    f.w[0] = x.x;
+    f.w[1] = x.y;
+  } else if constexpr (NW == 4) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    f.w[0] = x.x;
+    f.w[1] = x.y;
+    f.w[2] = x.z;
+    f.w[3] = x.w;
+  } else {
+    static_assert(NW == 8, "8, 16 or 32 bytes per lane per token");
+    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    const uint4 y = *reinterpret_cast<const uint4 *>(p + 16);
+    f.w[0] = x.x;
+    f.w[1] = x.y;
+    f.w[2] = x.z;
+    f.w[3] = x.w;
+    f.w[4] = y.x;
+    f.w[5] = y.y;
+    f.w[6] = y.z;
+    f.w[7] = y.w;
+  }
+}
+
+// Widen one lane's EPL stored elements to fp32 (bf16: low half first).
+template <typename T, int NW, int EPL>
+__device__ __forceinline__ void widen(const Frag<NW> &f, float (&x)[EPL]) {
+  if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = __uint_as_float(f.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      x[2 * i] = __uint_as_float(f.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(f.w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Partial dot of one lane's EPL dims: query (held as stored words) . key.
+template <typename T, int NW>
+__device__ __forceinline__ float partial_dot(const Frag<NW> &qw, const Frag<NW> &kw) {
+  float acc = 0.0f;
+  if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) acc = fmaf(__uint_as_float(qw.w[i]), __uint_as_float(kw.w[i]), acc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw.w[i]),
+                                            __builtin_bit_cast(bf16x2_t, kw.w[i]), acc, false);
+  }
+  return acc;
+}
+
+// Reduce-scatter of G partial dots across the 16 lanes of a row.  On entry
+// a[r] is this lane's partial for head r ^ sigma(lane), sigma(l) =
+// (l % QS) * HPL.  On exit a[t], t < HPL, is the full dot for head
+// sigma(lane) + t.  Split steps pair lanes differing in one quad bit; the
+// remaining bits are summed with rotations (all lanes then agree).
+template <int G>
+__device__ __forceinline__ void reduce_heads(float (&a)[G]) {
+  if constexpr (G == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] += dpp<kQuadXor2>(a[k + 4]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) a[k] += dpp<kQuadXor1>(a[k + 2]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      a[k] += dpp<kRowRor4>(a[k]);
+      a[k] += dpp<kRowRor8>(a[k]);
+    }
+  } else if constexpr (G == 4) {
+    a[0] += dpp<kQuadXor2>(a[2]);
+    a[1] += dpp<kQuadXor2>(a[3]);
+    a[0] += dpp<kQuadXor1>(a[1]);
+    a[0] += dpp<kRowRor4>(a[0]);
+    a[0] += dpp<kRowRor8>(a[0]);
+  } else if constexpr (G == 2) {
+    a[0] += dpp<kQuadXor1>(a[1]);
+    a[0] += dpp<kQuadXor2>(a[0]);
+    a[0] += dpp<kRowRor4>(a[0]);
+    a[0] += dpp<kRowRor8>(a[0]);
+  } else {
+    static_assert(G == 1, "group size 1, 2, 4 or 8");
+    a[0] += dpp<kQuadXor1>(a[0]);
+    a[0] += dpp<kQuadXor2>(a[0]);
+    a[0] += dpp<kRowRor4>(a[0]);
+    a[0] += dpp<kRowRor8>(a[0]);
+  }
+}
+
+// Value of head hh (held by quad lane hh / HPL in register hh % HPL) in every lane.
+template <int G, int HPL>
+__device__ __forceinline__ float head_value(const float (&v)[HPL], int hh) {
+  if constexpr (G == 1) {
+    return v[0];
+  } else {
+    const int k = hh / HPL, t = hh % HPL;
+    switch (k) {
+      case 0: return dpp<quad_bcast(0)>(v[t]);
+      case 1: return dpp<quad_bcast(1)>(v[t]);
+      case 2: return dpp<quad_bcast(2)>(v[t]);
+      default: return dpp<quad_bcast(3)>(v[t]);
+    }
+  }
+}
+
+template <typename T, int D, int B, int G>
+struct Cfg {
+  static constexpr int kElem = std::is_same_v<T, float> ? 4 : 2;
+  static constexpr int EPL = D / 16;             // elements per lane per token
+  static constexpr int VEC = EPL * kElem;        // bytes per lane per token
+  static constexpr int NW = VEC / 4;             // 32-bit words per lane per token
+  static constexpr int QS = G < 4 ? G : 4;       // quad lanes that own distinct heads
+  static constexpr int HPL = G / QS;             // heads owned per lane
+  static constexpr int CPB = B / kChunk;         // pipeline stages per block
+  static constexpr int64_t ROW = (int64_t)D * kElem;
+  static constexpr int64_t TILE = (int64_t)B * ROW;
+  static constexpr int64_t CHUNK = (int64_t)kChunk * ROW;
+  static constexpr int64_t STEP = 64 * VEC;      // bytes per load step (4 tokens)
+};
+
+template <typename T, int D, int B, int G>
+__global__ void __launch_bounds__(kThreads)
+decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
+              const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
+              int max_blocks_per_seq, const int32_t *__restrict__ context_lens, int num_q_heads,
+              float scale_log2, int max_context_len, int part_blocks, int max_parts, float *ws_o,
+              float *ws_ml, unsigned *ws_count) {
+  using C = Cfg<T, D, B, G>;
+  constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB;
+
+  __shared__ int s_tbl[kMaxPartitionBlocks];
+  __shared__ float s_o[kWaves][G][D];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ int s_flag;
+
+  const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane >> 4, col = lane & 15;
+
+  const int L = context_lens[s];
+  const bool bad = L < 0 || L > max_context_len || L > max_blocks_per_seq * B;
+  const int part_tokens = part_blocks * B;
+  const int nparts = (bad || L == 0) ? 1 : (L + part_tokens - 1) / part_tokens;
+  if (p >= nparts) return;
+
+  const int64_t head_row0 = ((int64_t)s * num_q_heads + (int64_t)h * G);  // first query/output row
+  if (bad) {
+    for (int i = tid; i < G * D; i += kThreads) out[head_row0 * D + i] = __builtin_nanf("");
+    return;
+  }
+
+  // ---- stage this partition's block ids in LDS (validated)
+  const int seq_blocks = (L + B - 1) / B;
+  const int blk_begin = p * part_blocks;
+  const int nblk = min(part_blocks, seq_blocks - blk_begin);
+  if (tid == 0) s_flag = 0;
+  __syncthreads();
+  for (int i = tid; i < nblk; i += kThreads) {
+    int b = tables[(int64_t)s * max_blocks_per_seq + blk_begin + i];
+    if (b < 0 || (int64_t)b >= num_blocks) {
+      s_flag = 1;
+      b = 0;
+    }
+    s_tbl[i] = b;
+  }
+
+  // ---- query registers: register r holds head r ^ sigma(lane), dims col*EPL ...
+  const int sigma = (lane % QS) * HPL;
+  Frag<NW> qf[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+    load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
+  __syncthreads();
+
+  float m[HPL], lsum[HPL], o[G][EPL];
+#pragma unroll
+  for (int t = 0; t < HPL; ++t) {
+    m[t] = kNegInf;
+    lsum[t] = 0.0f;
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[hh][e] = 0.0f;
+
+  const int nb_w = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int nch = nb_w * CPB;
+  const char *kv_head_base = pool + (int64_t)h * C::TILE;
+  const int64_t v_off = (int64_t)num_kv_heads * C::TILE;
+  const int lane_off = lane * C::VEC;
+
+  auto issue = [&](int ci, Frag<NW> (&kf)[4], Frag<NW> (&vf)[4]) {
+    const int lb = wave + (ci / CPB) * kWaves;
+    const int sub = ci % CPB;
+    const int phys = __builtin_amdgcn_readfirstlane(s_tbl[lb]);
+    const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_frag<NW>(kf[j], kp + j * C::STEP);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_frag<NW>(vf[j], kp + v_off + j * C::STEP);
+  };
+  auto process = [&](int ci, const Frag<NW> (&kf)[4], const Frag<NW> (&vf)[4]) {
+    const int tok0 = (blk_begin + wave + (ci / CPB) * kWaves) * B + (ci % CPB) * kChunk;
+    const bool partial = tok0 + kChunk > L;
+    // QK for the 4 tokens this row sees in the chunk
+    float sc[4][HPL];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) a[r] = partial_dot<T, NW>(qf[r], kf[j]);
+      reduce_heads<G>(a);
+      const bool valid = !partial || (tok0 + 4 * j + row < L);
+#pragma unroll
+      for (int t = 0; t < HPL; ++t) sc[j][t] = valid ? a[t] * scale_log2 : kNegInf;
+    }
+    // online softmax with a lazily raised running max
+    bool upd[HPL];
+    float m_new[HPL];
+    bool any_upd = false;
+#pragma unroll
+    for (int t = 0; t < HPL; ++t) {
+      const float cm = fmaxf(fmaxf(sc[0][t], sc[1][t]), fmaxf(sc[2][t], sc[3][t]));
+      const float mn = fmaxf(m[t], cm);
+      upd[t] = mn > m[t] + kRescaleThreshold;
+      m_new[t] = upd[t] ? mn : m[t];
+      any_upd |= upd[t];
+    }
+    if (__builtin_amdgcn_ballot_w64(any_upd) != 0) {
+      float alpha[HPL];
+#pragma unroll
+      for (int t = 0; t < HPL; ++t) {
+        alpha[t] = upd[t] ? fast_exp2(m[t] - m_new[t]) : 1.0f;
+        lsum[t] *= alpha[t];
+        m[t] = m_new[t];
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float a = head_value<G, HPL>(alpha, hh);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[hh][e] *= a;
+      }
+    }
+    float pr[4][HPL];
+#pragma unroll
+    for (int t = 0; t < HPL; ++t) {
+      const float ms = m[t] == kNegInf ? 0.0f : m[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr[j][t] = fast_exp2(sc[j][t] - ms);
+      lsum[t] += (pr[0][t] + pr[1][t]) + (pr[2][t] + pr[3][t]);
+    }
+    // PV
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v[EPL];
+      widen<T, NW, EPL>(vf[j], v);
+      if (partial && !(tok0 + 4 * j + row < L)) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[e] = 0.0f;
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float pb = head_value<G, HPL>(pr[j], hh);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pb, v[e], o[hh][e]);
+      }
+    }
+  };
+
+  // ---- main loop: double-buffered K/V chunks
+  {
+    Frag<NW> kA[4], vA[4], kB[4], vB[4];
+    if (nch > 0) issue(0, kA, vA);
+    for (int ci = 0; ci < nch; ci += 2) {
+      if (ci + 1 < nch) issue(ci + 1, kB, vB);
+      process(ci, kA, vA);
+      if (ci + 1 >= nch) break;
+      if (ci + 2 < nch) issue(ci + 2, kA, vA);
+      process(ci + 1, kB, vB);
+    }
+  }
+
+  // ---- merge the four row streams of this wave (partners lane ^ 16, lane ^ 32)
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    float a1[HPL], a2[HPL];
+#pragma unroll
+    for (int t = 0; t < HPL; ++t) {
+      const float m2 = __shfl_xor(m[t], off);
+      const float l2 = __shfl_xor(lsum[t], off);
+      const float M = fmaxf(m[t], m2);
+      const float Ms = M == kNegInf ? 0.0f : M;
+      a1[t] = fast_exp2(m[t] - Ms);
+      a2[t] = fast_exp2(m2 - Ms);
+      lsum[t] = a1[t] * lsum[t] + a2[t] * l2;
+      m[t] = M;
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float b1 = head_value<G, HPL>(a1, hh);
+      const float b2 = head_value<G, HPL>(a2, hh);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float o2 = __shfl_xor(o[hh][e], off);
+        o[hh][e] = b1 * o[hh][e] + b2 * o2;
+      }
+    }
+  }
+
+  // ---- merge the waves through LDS
+  if (row == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][hh][col * EPL + e] = o[hh][e];
+  }
+  if (lane < QS) {
+#pragma unroll
+    for (int t = 0; t < HPL; ++t) {
+      s_m[wave][lane * HPL + t] = m[t];
+      s_l[wave][lane * HPL + t] = lsum[t];
+    }
+  }
+  __syncthreads();
+  const bool poisoned = s_flag != 0;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i - hh * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][hh]);
+    const float Ms = M == kNegInf ? 0.0f : M;
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = fast_exp2(s_m[w][hh] - Ms);
+      num += a * s_o[w][hh][d];
+      den += a * s_l[w][hh];
+    }
+    if (poisoned) num = den = M = __builtin_nanf("");
+    if (nparts == 1) {
+      out[(head_row0 + hh) * D + d] = den > 0.0f ? num / den : (poisoned ? num : 0.0f);
+    } else {
+      const int64_t prow = (head_row0 + hh) * max_parts + p;
+      ws_o[prow * D + d] = num;
+      if (d == 0) {
+        ws_ml[prow * 2] = M;
+        ws_ml[prow * 2 + 1] = den;
+      }
+    }
+  }
+  if (nparts == 1) return;
+
+  // ---- split context: the last partition to finish combines all of them
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(&ws_count[(int64_t)s * num_kv_heads + h], 1u);
+    s_flag = (prev == (unsigned)(nparts - 1)) ? 2 : 3;
+  }
+  __syncthreads();
+  if (s_flag != 2) return;
+  __threadfence();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i - hh * D;
+    const int64_t prow0 = (head_row0 + hh) * max_parts;
+    float M = kNegInf;
+    for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, ws_ml[(prow0 + pp) * 2]);
+    const float Ms = M == kNegInf ? 0.0f : M;
+    float num = 0.0f, den = 0.0f;
+    for (int pp = 0; pp < nparts; ++pp) {
+      const float a = fast_exp2(ws_ml[(prow0 + pp) * 2] - Ms);
+      num += a * ws_o[(prow0 + pp) * D + d];
+      den += a * ws_ml[(prow0 + pp) * 2 + 1];
+    }
+    out[(head_row0 + hh) * D + d] = num / den;
+  }
+  if (tid == 0) ws_count[(int64_t)s * num_kv_heads + h] = 0u;
+}
+
+template <typename T, int D, int B, int G>
+hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid(a.num_partitions, a.pool.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_kernel<T, D, B, G>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
+                     static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
+                     a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,
+                     a.num_partitions, a.ws_o, a.ws_ml, a.ws_count);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int B>
+hipError_t dispatch_group(const DecodeArgs &a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_one<T, D, B, 1>(a, stream);
+    case 2: return launch_one<T, D, B, 2>(a, stream);
+    case 4: return launch_one<T, D, B, 4>(a, stream);
+    case 8: return launch_one<T, D, B, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t dispatch_block(const DecodeArgs &a, int group, hipStream_t stream) {
+  switch (a.pool.block_size) {
+    case 16: return dispatch_group<T, D, 16>(a, group, stream);
+    case 32: return dispatch_group<T, D, 32>(a, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t dispatch_dim(const DecodeArgs &a, int group, hipStream_t stream) {
+  switch (a.pool.head_dim) {
+    case 64: return dispatch_block<T, 64>(a, group, stream);
+    case 128: return dispatch_block<T, 128>(a, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool decode_supported(int dtype, int head_dim, int block_size, int group) {
+  return (dtype == PA_F32 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
+         (block_size == 16 || block_size == 32) && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.pool.num_kv_heads;
+  if (a.pool.dtype == PA_BF16) return dispatch_dim<bf16_tag>(a, group, stream);
+  if (a.pool.dtype == PA_F32) return dispatch_dim<float>(a, group, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

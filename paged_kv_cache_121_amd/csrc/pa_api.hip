@@ -1,0 +1,199 @@
+// C ABI of the paged KV-cache decode path: argument checks, workspace sizing,
+// partition choice and kernel launches.  No allocation, no synchronisation.
+
+#include <cmath>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr size_t kAlign = 256;
+// Automatic partitioning aims for at least this many workgroups per call.
+constexpr int64_t kTargetWorkgroups = 1024;
+// Automatic partitions hold at least this many tokens...
+constexpr int kMinAutoPartitionTokens = 256;
+// ...and at most this many, so long contexts still split evenly.
+constexpr int kMaxAutoPartitionTokens = 2048;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_pool(const pa_pool *p, PoolDesc *d) {
+  if (p == nullptr || p->base == nullptr) return PA_ERR_INVALID_ARG;
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (p->block_size != 16 && p->block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  d->base = static_cast<char *>(p->base);
+  d->num_blocks = p->num_blocks;
+  d->num_kv_heads = p->num_kv_heads;
+  d->block_size = p->block_size;
+  d->head_dim = p->head_dim;
+  d->dtype = p->dtype;
+  d->elem_bytes = p->dtype == PA_BF16 ? 2 : 4;
+  d->row_bytes = (int64_t)p->head_dim * d->elem_bytes;
+  d->tile_bytes = d->row_bytes * p->block_size;
+  d->block_bytes = 2 * d->tile_bytes * p->num_kv_heads;
+  // slot ids are int64 and block ids int32 in the tables
+  if (p->num_blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  const int64_t want_parts = pairs >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + pairs - 1) / pairs;
+  int64_t part = (max_context_len + want_parts - 1) / want_parts;
+  if (part < kMinAutoPartitionTokens) part = kMinAutoPartitionTokens;
+  if (part > kMaxAutoPartitionTokens) part = kMaxAutoPartitionTokens;
+  part = (part + block_size - 1) / block_size * block_size;
+  return (int)part;
+}
+
+// Resolves the partition size in tokens, or returns a negative status.
+int resolve_partition(const PoolDesc &pool, int num_seqs, int max_context_len, int partition_size) {
+  if (partition_size == 0)
+    return auto_partition_tokens(pool.block_size, num_seqs, pool.num_kv_heads, max_context_len);
+  if (partition_size < 0 || partition_size % pool.block_size != 0) return PA_ERR_INVALID_ARG;
+  if (partition_size / pool.block_size > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
+  return partition_size;
+}
+
+}  // namespace
+
+WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                        int num_partitions) {
+  WorkspaceLayout w{};
+  const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions;
+  w.o_off = 0;
+  w.ml_off = align_up(rows * head_dim * sizeof(float));
+  w.total = w.ml_off + align_up(rows * 2 * sizeof(float));
+  (void)num_kv_heads;
+  return w;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char *pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int pa_slot_mapping(const pa_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    int32_t num_seqs, const int32_t *seq_ids, const int32_t *positions,
+                    int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (seq_ids == nullptr || positions == nullptr || slot_mapping == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && max_blocks_per_seq > 0 && block_tables == nullptr) return PA_ERR_INVALID_ARG;
+  return status_of(launch_slot_mapping(d, block_tables, max_blocks_per_seq, num_seqs, seq_ids, positions,
+                                       slot_mapping, num_tokens, stream));
+}
+
+int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new, const int64_t *slot_mapping,
+                   int32_t num_tokens, hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return PA_ERR_INVALID_ARG;
+  return status_of(launch_cache_write(d, k_new, v_new, slot_mapping, num_tokens, stream));
+}
+
+int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks, int32_t num_pairs,
+                  hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PA_ERR_INVALID_ARG;
+  return status_of(launch_block_copy(d, src_blocks, dst_blocks, num_pairs, stream));
+}
+
+int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  return resolve_partition(d, num_seqs, max_context_len, 0);
+}
+
+size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_context_len, int32_t partition_size) {
+  PoolDesc d;
+  if (check_pool(pool, &d) != PA_OK) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
+  const int part = resolve_partition(d, num_seqs, max_context_len, partition_size);
+  if (part <= 0) return 0;
+  const int parts = (max_context_len + part - 1) / part;
+  if (parts <= 1) return 0;
+  return decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts).total;
+}
+
+int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+              float scale, int32_t max_context_len, int32_t partition_size, void *workspace,
+              size_t workspace_bytes, uint32_t *counters, hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * d.block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!decode_supported(d.dtype, d.head_dim, d.block_size, num_q_heads / d.num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (q == nullptr || out == nullptr || block_tables == nullptr || context_lens == nullptr)
+    return PA_ERR_INVALID_ARG;
+  const int part = resolve_partition(d, num_seqs, max_context_len, partition_size);
+  if (part < 0) return part;
+  const int parts = max_context_len == 0 ? 1 : (max_context_len + part - 1) / part;
+
+  DecodeArgs a{};
+  a.pool = d;
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.scale = scale;
+  a.max_context_len = max_context_len;
+  a.partition_blocks = part / d.block_size;
+  a.num_partitions = parts;
+  if (parts > 1) {
+    const WorkspaceLayout w = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts);
+    if (workspace == nullptr || workspace_bytes < w.total || counters == nullptr) return PA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return PA_ERR_WORKSPACE;
+    char *base = static_cast<char *>(workspace);
+    a.ws_o = reinterpret_cast<float *>(base + w.o_off);
+    a.ws_ml = reinterpret_cast<float *>(base + w.ml_off);
+    a.ws_count = counters;
+  }
+  return status_of(launch_decode(a, stream));
+}
+
+}  // extern "C"

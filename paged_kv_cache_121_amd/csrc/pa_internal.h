@@ -1,0 +1,65 @@
+// Internal declarations shared by the C ABI (pa_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+// Largest partition, in blocks, whose table entries one workgroup stages in LDS.
+constexpr int kMaxPartitionBlocks = 512;
+
+struct PoolDesc {
+  char *base;
+  int64_t num_blocks;
+  int num_kv_heads;
+  int block_size;
+  int head_dim;
+  int dtype;
+  int elem_bytes;
+  int64_t row_bytes;    // head_dim * elem_bytes: one token of one head, K or V
+  int64_t tile_bytes;   // block_size * row_bytes: one (block, head) K or V tile
+  int64_t block_bytes;  // 2 * num_kv_heads * tile_bytes: one physical block
+};
+
+struct DecodeArgs {
+  PoolDesc pool;
+  const void *q;
+  float *out;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *context_lens;
+  int num_seqs;
+  int num_q_heads;
+  float scale;
+  int max_context_len;
+  int partition_blocks;  // blocks per split-context partition
+  int num_partitions;    // ceil(max_context_len / (partition_blocks * block_size))
+  float *ws_o;           // [S][Hq][P][D] unnormalised partial outputs
+  float *ws_ml;          // [S][Hq][P][2] running max (log2 units) and sum
+  unsigned *ws_count;    // [S][Hkv] arrival counters, zero between calls
+};
+
+// Workspace layout of one decode call; every region 256-byte aligned.
+struct WorkspaceLayout {
+  size_t o_off, ml_off, total;
+};
+WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                        int num_partitions);
+
+hipError_t launch_slot_mapping(const PoolDesc &pool, const int32_t *tables, int max_blocks_per_seq,
+                               int num_seqs, const int32_t *seq_ids, const int32_t *positions,
+                               int64_t *slots, int num_tokens, hipStream_t stream);
+hipError_t launch_cache_write(const PoolDesc &pool, const void *k_new, const void *v_new,
+                              const int64_t *slots, int num_tokens, hipStream_t stream);
+hipError_t launch_block_copy(const PoolDesc &pool, const int32_t *src, const int32_t *dst, int num_pairs,
+                             hipStream_t stream);
+// Returns hipErrorInvalidValue when no kernel is built for the shape.
+hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream);
+bool decode_supported(int dtype, int head_dim, int block_size, int group);
+
+}  // namespace pa
