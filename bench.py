@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the oracle's timed sample")
     ap.add_argument("--skip-check", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
+                    help="instead of the benchmark: run pa_block_copy over PAIRS distinct block pairs "
+                         "(known bytes) 5 times, for scaling hardware byte counters")
     return ap.parse_args()
 
 
@@ -75,6 +78,22 @@ def cpu_baseline(w, n_seqs: int):
             "seq_layers_per_s": len(sel) / dt}
 
 
+def calibrate_copy(pairs: int, dev):
+    """pa_block_copy of ``pairs`` distinct 64 KiB blocks (bf16, 8 KV heads, B16, D128):
+    reads and writes exactly pairs * 65536 bytes per launch."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    pool = pa.PagedKVPool(torch.zeros((2 * pairs, 2, 8, 16, 128), dtype=torch.bfloat16, device=dev))
+    src = torch.arange(0, pairs, dtype=torch.int32, device=dev)
+    dst = torch.arange(pairs, 2 * pairs, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        pa.pa_block_copy(pool, src, dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_pairs": pairs, "bytes_read_per_launch": pairs * 65536,
+                      "bytes_written_per_launch": pairs * 65536}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -92,6 +111,9 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, dev)
+        return
     t_gen = time.perf_counter()
     w = make_config(args.workload)
     t_gen = time.perf_counter() - t_gen
@@ -117,7 +139,6 @@ def main():
     part = args.partition_size or pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads, max_len)
     nbytes = pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, max_len, part)
     workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    counters = torch.zeros(w.num_seqs * w.num_kv_heads, dtype=torch.int32, device=dev)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     slots = torch.empty(len(st.write_seq), dtype=torch.int64, device=dev)
     scale = float(w.scale)
@@ -125,7 +146,7 @@ def main():
 
     def decode():
         pa.pa_decode(pool, q, tables, lens, scale=scale, max_context_len=max_len, partition_size=part,
-                     out=out, workspace=workspace, counters=counters)
+                     out=out, workspace=workspace)
 
     def step():
         if len(st.cow_src):

@@ -148,13 +148,9 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
  *                  pa_decode_workspace_size() bytes, 256-byte aligned (may
  *                  be NULL when that size is 0).  Contents need no
  *                  initialisation.
- *   counters     : uint32 [num_seqs][num_kv_heads] arrival counters of the
- *                  split-context combine (may be NULL when the workspace
- *                  size is 0).  They must be zero before the first call;
- *                  every call leaves them zero again, so one zeroed buffer
- *                  large enough for the biggest batch can be reused.
- * Calls sharing a workspace or counters must not overlap in time (calls on
- * one stream never do).  Query head hq reads KV head
+ * Calls sharing a workspace must not overlap in time (calls on one stream
+ * never do).  A call launches one kernel, plus a small combine kernel when
+ * some sequence spans more than one partition.  Query head hq reads KV head
  * hq / (num_q_heads / num_kv_heads); the group size must be 1, 2, 4 or 8.
  * Output rows of a sequence with a context length of 0 are zero; rows of a
  * sequence whose context length is negative, exceeds max_context_len or its
@@ -164,7 +160,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
 int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
               int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
-              void *workspace, size_t workspace_bytes, uint32_t *counters, hipStream_t stream);
+              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *pa_status_str(int status);

@@ -24,7 +24,6 @@ import threading
 __all__ = [
     "PaError",
     "PagedKVPool",
-    "decode_counters",
     "library_path",
     "load_library",
     "pa_block_copy",
@@ -72,7 +71,7 @@ _SIGNATURES = {
     "pa_block_copy": (_I32, [_POOLP, _VP, _VP, _I32, _VP]),
     "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
     "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
-    "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _VP, _SZ, _VP, _VP]),
+    "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _VP, _SZ, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -233,7 +232,6 @@ def pa_decode_workspace_size(pool: PagedKVPool, num_seqs: int, num_q_heads: int,
 
 
 _workspaces: dict = {}
-_counters: dict = {}
 
 
 def _workspace(device, nbytes: int):
@@ -247,24 +245,8 @@ def _workspace(device, nbytes: int):
     return buf
 
 
-def decode_counters(device, count: int):
-    """Zeroed uint32 arrival counters (as int32) of at least ``count`` entries per device.
-
-    The decode kernels leave them at zero, so they are zeroed only when
-    (re)allocated and can serve every later call on the device's stream.
-    """
-    torch = _torch()
-    key = str(device)
-    buf = _counters.get(key)
-    if buf is None or buf.numel() < count:
-        buf = torch.zeros(max(count, 4096), dtype=torch.int32, device=device)
-        _counters[key] = buf
-    return buf
-
-
 def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | None = None,
-              max_context_len: int | None = None, partition_size: int = 0, out=None, workspace=None,
-              counters=None):
+              max_context_len: int | None = None, partition_size: int = 0, out=None, workspace=None):
     """Paged decode attention; returns float32 ``[S][Hq][D]``.
 
     ``max_context_len`` defaults to the table width times the block size (a
@@ -291,14 +273,9 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
         ws = _workspace(dev, need) if need else None
     else:
         ws = _dev_tensor(workspace, "workspace", torch.uint8, 1, dev)
-    if counters is None:
-        cnt = decode_counters(dev, S * pool.num_kv_heads) if need else None
-    else:
-        cnt = _dev_tensor(counters, "counters", torch.int32, 1, dev)
-        _need(cnt.numel() >= S * pool.num_kv_heads, "counters needs num_seqs * num_kv_heads entries")
     lib = load_library()
     _check(lib.pa_decode(pool.desc, _ptr(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
                          _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size),
                          _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
-                         _ptr(cnt) if cnt is not None else None, _stream(q)), "pa_decode")
+                         _stream(q)), "pa_decode")
     return out

@@ -35,11 +35,11 @@
 // Masking: tokens at or past the context length get score -inf and value 0
 //   (selected, never multiplied), so poisoned padding cannot leak in.
 // Split context: when a sequence spans more than one partition, every
-//   partition writes (max, sum, unnormalised output) to the workspace and
-//   the last workgroup to arrive (device-scope counter) combines them in
-//   partition order and writes the output, then zeroes the counter.  The
-//   combination order depends only on logical positions, so results are
-//   identical under any physical placement of the blocks.
+//   partition writes (max, sum, unnormalised output) to the workspace and a
+//   second kernel combines the partitions of each (sequence, head) in
+//   partition order.  The kernel boundary makes the partials visible without
+//   device-wide fences.  The combination order depends only on logical
+//   positions, so results are identical under any physical placement.
 
 #include <type_traits>
 
@@ -189,6 +189,16 @@ __device__ __forceinline__ float head_value(const float (&v)[HPL], int hh) {
   }
 }
 
+// Partitions a sequence of length L spans (0 when its outputs are set by
+// the first partition alone: empty or invalid context).  Both kernels use
+// this one definition.
+__device__ __forceinline__ int partitions_of(int L, int max_context_len, int max_tokens_per_row,
+                                             int part_tokens) {
+  if (L < 0 || L > max_context_len || L > max_tokens_per_row) return -1;  // invalid: NaN rows
+  if (L == 0) return 0;
+  return (L + part_tokens - 1) / part_tokens;
+}
+
 template <typename T, int D, int B, int G>
 struct Cfg {
   static constexpr int kElem = std::is_same_v<T, float> ? 4 : 2;
@@ -209,8 +219,8 @@ __global__ void __launch_bounds__(kThreads)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
               int max_blocks_per_seq, const int32_t *__restrict__ context_lens, int num_q_heads,
-              float scale_log2, int max_context_len, int part_blocks, int max_parts, float *ws_o,
-              float *ws_ml, unsigned *ws_count) {
+              float scale_log2, int max_context_len, int part_blocks, int max_parts,
+              float *__restrict__ ws_o, float *__restrict__ ws_ml) {
   using C = Cfg<T, D, B, G>;
   constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB;
 
@@ -218,20 +228,21 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ int s_flag;
+  __shared__ int s_poison;
 
   const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int row = lane >> 4, col = lane & 15;
 
   const int L = context_lens[s];
-  const bool bad = L < 0 || L > max_context_len || L > max_blocks_per_seq * B;
   const int part_tokens = part_blocks * B;
-  const int nparts = (bad || L == 0) ? 1 : (L + part_tokens - 1) / part_tokens;
+  const int np = partitions_of(L, max_context_len, max_blocks_per_seq * B, part_tokens);
+  const int nparts = np < 1 ? 1 : np;
   if (p >= nparts) return;
 
   const int64_t head_row0 = ((int64_t)s * num_q_heads + (int64_t)h * G);  // first query/output row
-  if (bad) {
+  if (np < 0) {
     for (int i = tid; i < G * D; i += kThreads) out[head_row0 * D + i] = __builtin_nanf("");
     return;
   }
@@ -240,12 +251,12 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   const int seq_blocks = (L + B - 1) / B;
   const int blk_begin = p * part_blocks;
   const int nblk = min(part_blocks, seq_blocks - blk_begin);
-  if (tid == 0) s_flag = 0;
+  if (tid == 0) s_poison = 0;
   __syncthreads();
   for (int i = tid; i < nblk; i += kThreads) {
     int b = tables[(int64_t)s * max_blocks_per_seq + blk_begin + i];
     if (b < 0 || (int64_t)b >= num_blocks) {
-      s_flag = 1;
+      s_poison = 1;
       b = 0;
     }
     s_tbl[i] = b;
@@ -354,17 +365,23 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     }
   };
 
-  // ---- main loop: double-buffered K/V chunks
-  {
+  // ---- main loop: double-buffered K/V chunks, two per iteration with no
+  // exit in between.  Every load is issued unconditionally (the prefetch past
+  // the end re-reads the last chunk, an L2 hit), so the compiler's wait
+  // counts at each use cover exactly the loads issued before it: each
+  // process() waits for its own chunk while the next one is in flight.
+  if (nch > 0) {
     Frag<NW> kA[4], vA[4], kB[4], vB[4];
-    if (nch > 0) issue(0, kA, vA);
-    for (int ci = 0; ci < nch; ci += 2) {
-      if (ci + 1 < nch) issue(ci + 1, kB, vB);
+    const int last = nch - 1;
+    issue(0, kA, vA);
+    int ci = 0;
+    for (; ci < last; ci += 2) {
+      issue(ci + 1, kB, vB);
       process(ci, kA, vA);
-      if (ci + 1 >= nch) break;
-      if (ci + 2 < nch) issue(ci + 2, kA, vA);
+      issue(min(ci + 2, last), kA, vA);
       process(ci + 1, kB, vB);
     }
+    if (ci == last) process(ci, kA, vA);
   }
 
   // ---- merge the four row streams of this wave (partners lane ^ 16, lane ^ 32)
@@ -409,7 +426,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     }
   }
   __syncthreads();
-  const bool poisoned = s_flag != 0;
+  const bool poisoned = s_poison != 0;
   for (int i = tid; i < G * D; i += kThreads) {
     const int hh = i / D, d = i - hh * D;
     float M = kNegInf;
@@ -435,33 +452,31 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
       }
     }
   }
-  if (nparts == 1) return;
+}
 
-  // ---- split context: the last partition to finish combines all of them
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&ws_count[(int64_t)s * num_kv_heads + h], 1u);
-    s_flag = (prev == (unsigned)(nparts - 1)) ? 2 : 3;
+// Combine the partitions of one (sequence, query head): D threads, one per
+// output element, partitions taken in order.
+template <int D>
+__global__ void __launch_bounds__(D)
+combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
+               const int32_t *__restrict__ context_lens, int num_q_heads, int max_context_len,
+               int max_tokens_per_row, int part_tokens, int max_parts) {
+  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int np = partitions_of(context_lens[s], max_context_len, max_tokens_per_row, part_tokens);
+  if (np <= 1) return;  // written by the decode kernel itself
+  const int64_t row = (int64_t)s * num_q_heads + hq;
+  const float *ml = ws_ml + row * max_parts * 2;
+  const float *o = ws_o + row * max_parts * D + d;
+  float M = kNegInf;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  const float Ms = M == kNegInf ? 0.0f : M;
+  float num = 0.0f, den = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    const float a = fast_exp2(ml[2 * p] - Ms);
+    num += a * o[(int64_t)p * D];
+    den += a * ml[2 * p + 1];
   }
-  __syncthreads();
-  if (s_flag != 2) return;
-  __threadfence();
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int hh = i / D, d = i - hh * D;
-    const int64_t prow0 = (head_row0 + hh) * max_parts;
-    float M = kNegInf;
-    for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, ws_ml[(prow0 + pp) * 2]);
-    const float Ms = M == kNegInf ? 0.0f : M;
-    float num = 0.0f, den = 0.0f;
-    for (int pp = 0; pp < nparts; ++pp) {
-      const float a = fast_exp2(ws_ml[(prow0 + pp) * 2] - Ms);
-      num += a * ws_o[(prow0 + pp) * D + d];
-      den += a * ws_ml[(prow0 + pp) * 2 + 1];
-    }
-    out[(head_row0 + hh) * D + d] = num / den;
-  }
-  if (tid == 0) ws_count[(int64_t)s * num_kv_heads + h] = 0u;
+  out[row * D + d] = num / den;
 }
 
 template <typename T, int D, int B, int G>
@@ -471,7 +486,12 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,
-                     a.num_partitions, a.ws_o, a.ws_ml, a.ws_count);
+                     a.num_partitions, a.ws_o, a.ws_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_partitions == 1) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a.ws_o, a.ws_ml,
+                     a.out, a.context_lens, a.num_q_heads, a.max_context_len, a.max_blocks_per_seq * B,
+                     a.partition_blocks * B, a.num_partitions);
   return hipGetLastError();
 }
 

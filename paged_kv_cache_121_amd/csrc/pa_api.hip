@@ -10,12 +10,15 @@ namespace pa {
 namespace {
 
 constexpr size_t kAlign = 256;
-// Automatic partitioning aims for at least this many workgroups per call.
-constexpr int64_t kTargetWorkgroups = 1024;
-// Automatic partitions hold at least this many tokens...
+// Automatic partitioning.  A call wants at least kMinWorkgroups workgroups
+// (two per compute unit) so every CU streams; few (sequence, KV head) pairs
+// are therefore split into equal partitions.  Batches with many pairs are
+// likely to mix short and long contexts, so their partitions are capped at
+// kSkewedPartitionTokens to keep one long sequence from becoming the tail.
+constexpr int64_t kMinWorkgroups = 512;
+constexpr int64_t kManyPairs = 1024;
+constexpr int kSkewedPartitionTokens = 2048;
 constexpr int kMinAutoPartitionTokens = 256;
-// ...and at most this many, so long contexts still split evenly.
-constexpr int kMaxAutoPartitionTokens = 2048;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -45,11 +48,13 @@ int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
 int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  const int64_t want_parts = pairs >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + pairs - 1) / pairs;
+  const int64_t want_parts = pairs >= kMinWorkgroups ? 1 : (kMinWorkgroups + pairs - 1) / pairs;
   int64_t part = (max_context_len + want_parts - 1) / want_parts;
+  if (pairs >= kManyPairs && part > kSkewedPartitionTokens) part = kSkewedPartitionTokens;
   if (part < kMinAutoPartitionTokens) part = kMinAutoPartitionTokens;
-  if (part > kMaxAutoPartitionTokens) part = kMaxAutoPartitionTokens;
   part = (part + block_size - 1) / block_size * block_size;
+  const int64_t cap = (int64_t)kMaxPartitionBlocks * block_size;
+  if (part > cap) part = cap;
   return (int)part;
 }
 
@@ -152,7 +157,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
 int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
               float scale, int32_t max_context_len, int32_t partition_size, void *workspace,
-              size_t workspace_bytes, uint32_t *counters, hipStream_t stream) {
+              size_t workspace_bytes, hipStream_t stream) {
   PoolDesc d;
   const int st = check_pool(pool, &d);
   if (st != PA_OK) return st;
@@ -186,12 +191,11 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
   a.num_partitions = parts;
   if (parts > 1) {
     const WorkspaceLayout w = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts);
-    if (workspace == nullptr || workspace_bytes < w.total || counters == nullptr) return PA_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return PA_ERR_WORKSPACE;
     char *base = static_cast<char *>(workspace);
     a.ws_o = reinterpret_cast<float *>(base + w.o_off);
     a.ws_ml = reinterpret_cast<float *>(base + w.ml_off);
-    a.ws_count = counters;
   }
   return status_of(launch_decode(a, stream));
 }

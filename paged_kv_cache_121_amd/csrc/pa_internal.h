@@ -41,7 +41,6 @@ struct DecodeArgs {
   int num_partitions;    // ceil(max_context_len / (partition_blocks * block_size))
   float *ws_o;           // [S][Hq][P][D] unnormalised partial outputs
   float *ws_ml;          // [S][Hq][P][2] running max (log2 units) and sum
-  unsigned *ws_count;    // [S][Hkv] arrival counters, zero between calls
 };
 
 // Workspace layout of one decode call; every region 256-byte aligned.
