@@ -20,7 +20,8 @@ import numpy as np
 
 METRIC = "decode attention KV-read GB/s (and % HBM peak); sequences·layers/sec"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_traffic.json")
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_qwen3_8b_b64_hbm_traffic.md")
 
 
 def parse():
@@ -53,7 +54,11 @@ def measured_traffic(workload: int, partition_size: int):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
-        t = json.load(f)
+        text = f.read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    t = json.loads(text[start + 7:text.index("```", start + 7)])
     e = t.get(f"workload{workload}")
     if not e or e.get("decode_source_sha256_16") != kernel_source_digest() or e.get("partition_size") != partition_size:
         return None
