@@ -48,7 +48,22 @@
 namespace pa {
 namespace {
 
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 1
+#endif
+#ifndef PA_DECODE_NT_LOADS
+#define PA_DECODE_NT_LOADS 1
+#endif
+
 constexpr int kWaves = 4;
+// Chunks in flight ahead of the one being processed.  Measured on the
+// Qwen3-8B batch-64 layer: 1 ahead already hides the latency (2 ahead was
+// 3 % slower, it costs 20 more VGPRs).
+constexpr int kPrefetch = PA_DECODE_PREFETCH;
+// K/V are read once per step: marking the loads non-temporal keeps them from
+// displacing reusable lines in L2 and raised decode bandwidth from 5.8 to
+// 6.4 TB/s on the same workload.
+constexpr bool kNtLoads = PA_DECODE_NT_LOADS != 0;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 16;                    // tokens per pipeline stage
 constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
@@ -76,22 +91,31 @@ struct Frag {
   uint32_t w[NW];
 };
 
-template <int NW>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename V, bool NT>
+__device__ __forceinline__ V load_vec(const char *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+  return *reinterpret_cast<const V *>(p);
+}
+
+template <int NW, bool NT = false>
 __device__ __forceinline__ void load_frag(Frag<NW> &f, const char *p) {
   if constexpr (NW == 2) {
-    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    const u32x2 x = load_vec<u32x2, NT>(p);
     f.w[0] = x.x;
     f.w[1] = x.y;
   } else if constexpr (NW == 4) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    const u32x4 x = load_vec<u32x4, NT>(p);
     f.w[0] = x.x;
     f.w[1] = x.y;
     f.w[2] = x.z;
     f.w[3] = x.w;
   } else {
     static_assert(NW == 8, "8, 16 or 32 bytes per lane per token");
-    const uint4 x = *reinterpret_cast<const uint4 *>(p);
-    const uint4 y = *reinterpret_cast<const uint4 *>(p + 16);
+    const u32x4 x = load_vec<u32x4, NT>(p);
+    const u32x4 y = load_vec<u32x4, NT>(p + 16);
     f.w[0] = x.x;
     f.w[1] = x.y;
     f.w[2] = x.z;
@@ -293,9 +317,9 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     const int phys = __builtin_amdgcn_readfirstlane(s_tbl[lb]);
     const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW>(kf[j], kp + j * C::STEP);
+    for (int j = 0; j < 4; ++j) load_frag<NW, kNtLoads>(kf[j], kp + j * C::STEP);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW>(vf[j], kp + v_off + j * C::STEP);
+    for (int j = 0; j < 4; ++j) load_frag<NW, kNtLoads>(vf[j], kp + v_off + j * C::STEP);
   };
   auto process = [&](int ci, const Frag<NW> (&kf)[4], const Frag<NW> (&vf)[4]) {
     const int tok0 = (blk_begin + wave + (ci / CPB) * kWaves) * B + (ci % CPB) * kChunk;
@@ -370,18 +394,40 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // the end re-reads the last chunk, an L2 hit), so the compiler's wait
   // counts at each use cover exactly the loads issued before it: each
   // process() waits for its own chunk while the next one is in flight.
-  if (nch > 0) {
-    Frag<NW> kA[4], vA[4], kB[4], vB[4];
-    const int last = nch - 1;
-    issue(0, kA, vA);
-    int ci = 0;
-    for (; ci < last; ci += 2) {
-      issue(ci + 1, kB, vB);
-      process(ci, kA, vA);
-      issue(min(ci + 2, last), kA, vA);
-      process(ci + 1, kB, vB);
+  if constexpr (kPrefetch == 1) {
+    if (nch > 0) {
+      Frag<NW> kA[4], vA[4], kB[4], vB[4];
+      const int last = nch - 1;
+      issue(0, kA, vA);
+      int ci = 0;
+      for (; ci < last; ci += 2) {
+        issue(ci + 1, kB, vB);
+        process(ci, kA, vA);
+        issue(min(ci + 2, last), kA, vA);
+        process(ci + 1, kB, vB);
+      }
+      if (ci == last) process(ci, kA, vA);
     }
-    if (ci == last) process(ci, kA, vA);
+  } else {
+    static_assert(kPrefetch == 2, "prefetch depth 1 or 2");
+    // three buffers, two chunks in flight while one is processed
+    if (nch > 0) {
+      Frag<NW> kA[4], vA[4], kB[4], vB[4], kC[4], vC[4];
+      const int last = nch - 1;
+      issue(0, kA, vA);
+      issue(min(1, last), kB, vB);
+      int ci = 0;
+      for (; ci + 2 <= last; ci += 3) {
+        issue(ci + 2, kC, vC);
+        process(ci, kA, vA);
+        issue(min(ci + 3, last), kA, vA);
+        process(ci + 1, kB, vB);
+        issue(min(ci + 4, last), kB, vB);
+        process(ci + 2, kC, vC);
+      }
+      if (ci <= last) process(ci, kA, vA);
+      if (ci + 1 <= last) process(ci + 1, kB, vB);
+    }
   }
 
   // ---- merge the four row streams of this wave (partners lane ^ 16, lane ^ 32)
