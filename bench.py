@@ -149,9 +149,11 @@ def main():
     scale = float(w.scale)
     torch.cuda.synchronize()
 
+    keep_cached = bool(w.meta.get("prefix_tokens"))  # shared prefix blocks: keep K/V in L2
+
     def decode():
         pa.pa_decode(pool, q, tables, lens, scale=scale, max_context_len=max_len, partition_size=part,
-                     out=out, workspace=workspace)
+                     out=out, workspace=workspace, keep_cached=keep_cached)
 
     def step():
         if len(st.cow_src):
@@ -229,6 +231,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": w.num_blocks,
             "context_tokens": int(st.context_lens.sum()), "max_context_len": max_len,
             "partition_size": part, "kv_bytes_per_step": kv_bytes,
+            "kv_cache_policy": "keep cached (shared blocks)" if keep_cached else "stream (non-temporal)",
         },
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_gbs": round(achieved, 1),

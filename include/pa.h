@@ -52,6 +52,18 @@ typedef enum {
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
 /*
+ * pa_decode flags.
+ *   PA_DECODE_STREAM (0): K/V loads carry the non-temporal hint.  Each byte
+ *     of K/V is read once per step, so nothing worth keeping is evicted from
+ *     L2 (the faster choice when sequences do not share blocks).
+ *   PA_DECODE_KEEP_CACHED: K/V loads use the normal cache policy.  Pass it
+ *     when sequences of the batch share physical blocks (a common prefix,
+ *     [AINEW] copy-on-write passage; [TSS] "Sharing a prefix"): the later
+ *     readers of a shared block then hit in L2.
+ */
+typedef enum { PA_DECODE_STREAM = 0, PA_DECODE_KEEP_CACHED = 1 } pa_decode_flags;
+
+/*
  * The physical block pool ([AINEW] "PagedAttention in one picture";
  * [TSS] "Paging": fixed-size blocks carved out of the cache memory).
  * `base` points at num_blocks * 2 * num_kv_heads * block_size * head_dim
@@ -144,6 +156,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
  *   partition_size  : tokens per split-context partition; 0 = automatic;
  *                  else a positive multiple of block_size, at most 512
  *                  blocks.
+ *   flags        : PA_DECODE_STREAM or PA_DECODE_KEEP_CACHED (see above).
  *   workspace    : scratch for split-context partial results, at least
  *                  pa_decode_workspace_size() bytes, 256-byte aligned (may
  *                  be NULL when that size is 0).  Contents need no
@@ -160,7 +173,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
 int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
               int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
-              void *workspace, size_t workspace_bytes, hipStream_t stream);
+              int32_t flags, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *pa_status_str(int status);

@@ -37,6 +37,7 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 PA_F32, PA_BF16 = 0, 1
+PA_DECODE_STREAM, PA_DECODE_KEEP_CACHED = 0, 1
 
 
 def library_path() -> str:
@@ -71,7 +72,7 @@ _SIGNATURES = {
     "pa_block_copy": (_I32, [_POOLP, _VP, _VP, _I32, _VP]),
     "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
     "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
-    "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _VP, _SZ, _VP]),
+    "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -246,11 +247,14 @@ def _workspace(device, nbytes: int):
 
 
 def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | None = None,
-              max_context_len: int | None = None, partition_size: int = 0, out=None, workspace=None):
+              max_context_len: int | None = None, partition_size: int = 0, out=None, workspace=None,
+              keep_cached: bool = False):
     """Paged decode attention; returns float32 ``[S][Hq][D]``.
 
     ``max_context_len`` defaults to the table width times the block size (a
     bound known without reading ``context_lens`` back from the device).
+    ``keep_cached=True`` passes PA_DECODE_KEEP_CACHED (batches whose
+    sequences share physical blocks).
     """
     torch = _torch()
     dev = pool.device
@@ -276,6 +280,6 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
     lib = load_library()
     _check(lib.pa_decode(pool.desc, _ptr(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
                          _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size),
-                         _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
+                         PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM, _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
                          _stream(q)), "pa_decode")
     return out

@@ -51,19 +51,12 @@ namespace {
 #ifndef PA_DECODE_PREFETCH
 #define PA_DECODE_PREFETCH 1
 #endif
-#ifndef PA_DECODE_NT_LOADS
-#define PA_DECODE_NT_LOADS 1
-#endif
 
 constexpr int kWaves = 4;
 // Chunks in flight ahead of the one being processed.  Measured on the
 // Qwen3-8B batch-64 layer: 1 ahead already hides the latency (2 ahead was
 // 3 % slower, it costs 20 more VGPRs).
 constexpr int kPrefetch = PA_DECODE_PREFETCH;
-// K/V are read once per step: marking the loads non-temporal keeps them from
-// displacing reusable lines in L2 and raised decode bandwidth from 5.8 to
-// 6.4 TB/s on the same workload.
-constexpr bool kNtLoads = PA_DECODE_NT_LOADS != 0;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 16;                    // tokens per pipeline stage
 constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
@@ -238,7 +231,12 @@ struct Cfg {
   static constexpr int64_t STEP = 64 * VEC;      // bytes per load step (4 tokens)
 };
 
-template <typename T, int D, int B, int G>
+// NT: K/V loads carry the non-temporal hint.  K/V are read once per step, so
+// streaming them keeps them from displacing reusable lines in L2; measured on
+// the Qwen3-8B batch-64 layer it raised decode bandwidth from 5.8 to 6.4
+// TB/s.  Batches whose sequences share blocks want the normal policy instead
+// (the later readers of a shared block hit in L2).
+template <typename T, int D, int B, int G, bool NT>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
@@ -317,9 +315,9 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     const int phys = __builtin_amdgcn_readfirstlane(s_tbl[lb]);
     const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW, kNtLoads>(kf[j], kp + j * C::STEP);
+    for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp + j * C::STEP);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW, kNtLoads>(vf[j], kp + v_off + j * C::STEP);
+    for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp + v_off + j * C::STEP);
   };
   auto process = [&](int ci, const Frag<NW> (&kf)[4], const Frag<NW> (&vf)[4]) {
     const int tok0 = (blk_begin + wave + (ci / CPB) * kWaves) * B + (ci % CPB) * kChunk;
@@ -528,7 +526,8 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
 template <typename T, int D, int B, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid(a.num_partitions, a.pool.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<T, D, B, G>), grid, dim3(kThreads), 0, stream,
+  auto kernel = a.stream_loads ? decode_kernel<T, D, B, G, true> : decode_kernel<T, D, B, G, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,

@@ -156,7 +156,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
 
 int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-              float scale, int32_t max_context_len, int32_t partition_size, void *workspace,
+              float scale, int32_t max_context_len, int32_t partition_size, int32_t flags, void *workspace,
               size_t workspace_bytes, hipStream_t stream) {
   PoolDesc d;
   const int st = check_pool(pool, &d);
@@ -165,6 +165,7 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (flags & ~PA_DECODE_KEEP_CACHED) return PA_ERR_INVALID_ARG;
   if ((int64_t)max_blocks_per_seq * d.block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if (!decode_supported(d.dtype, d.head_dim, d.block_size, num_q_heads / d.num_kv_heads))
@@ -189,6 +190,7 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
   a.max_context_len = max_context_len;
   a.partition_blocks = part / d.block_size;
   a.num_partitions = parts;
+  a.stream_loads = (flags & PA_DECODE_KEEP_CACHED) == 0;
   if (parts > 1) {
     const WorkspaceLayout w = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts);
     if (workspace == nullptr || workspace_bytes < w.total) return PA_ERR_WORKSPACE;

@@ -39,6 +39,7 @@ struct DecodeArgs {
   int max_context_len;
   int partition_blocks;  // blocks per split-context partition
   int num_partitions;    // ceil(max_context_len / (partition_blocks * block_size))
+  bool stream_loads;     // non-temporal K/V loads (PA_DECODE_STREAM)
   float *ws_o;           // [S][Hq][P][D] unnormalised partial outputs
   float *ws_ml;          // [S][Hq][P][2] running max (log2 units) and sum
 };

@@ -40,7 +40,8 @@ def device_pool(w) -> pa.PagedKVPool:
     return pa.PagedKVPool(to_dev(w.pool, w.dtype))
 
 
-def run_step(w, pool: pa.PagedKVPool, tables_dev, k: int, partition_size: int = 0, max_context_len=None):
+def run_step(w, pool: pa.PagedKVPool, tables_dev, k: int, partition_size: int = 0, max_context_len=None,
+             keep_cached=None):
     """One step of workload ``w`` on the GPU: COW copies, slot mapping, cache write, decode."""
     st = w.steps[k]
     if len(st.cow_src):
@@ -49,8 +50,10 @@ def run_step(w, pool: pa.PagedKVPool, tables_dev, k: int, partition_size: int = 
     pa.pa_cache_write(pool, to_dev(st.k_new, w.dtype), to_dev(st.v_new, w.dtype), slots)
     lens = i32(st.context_lens)
     mcl = int(st.context_lens.max()) if max_context_len is None else max_context_len
+    if keep_cached is None:  # workloads that share blocks keep K/V cached, the others stream
+        keep_cached = bool(w.meta.get("prefix_tokens"))
     out = pa.pa_decode(pool, to_dev(st.q, w.dtype), tables_dev, lens, scale=float(w.scale),
-                       max_context_len=mcl, partition_size=partition_size)
+                       max_context_len=mcl, partition_size=partition_size, keep_cached=keep_cached)
     return slots, out
 
 

@@ -58,13 +58,14 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.pa_cache_write(ref(good), None, None, None, 0, None) == 0
     assert lib.pa_block_copy(ref(good), None, None, 0, None) == 0
     assert lib.pa_slot_mapping(ref(good), None, 4, 3, None, None, None, 0, None) == 0
-    assert lib.pa_decode(ref(good), None, None, None, 4, None, 0, 4, 0.125, 48, 0, None, 0, None) == 0
+    assert lib.pa_decode(ref(good), None, None, None, 4, None, 0, 4, 0.125, 48, 0, 0, None, 0, None) == 0
     # decode: group size 3 unsupported, Hq not a multiple of Hkv, bad partition size, missing workspace
-    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 12, 0.1, 48, 0, None, 0, None) == -2
-    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 6, 0.1, 48, 0, None, 0, None) == -1
-    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 24, None, 0, None) == -1
-    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, float("nan"), 48, 0, None, 0, None) == -1
-    assert lib.pa_decode(ref(good), 1, 1, 1, 64, 1, 3, 4, 0.1, 1024, 16, None, 0, None) == -3
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 12, 0.1, 48, 0, 0, None, 0, None) == -2
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 6, 0.1, 48, 0, 0, None, 0, None) == -1
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 24, 0, None, 0, None) == -1
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, float("nan"), 48, 0, 0, None, 0, None) == -1
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 0, 2, None, 0, None) == -1  # unknown flag
+    assert lib.pa_decode(ref(good), 1, 1, 1, 64, 1, 3, 4, 0.1, 1024, 16, 0, None, 0, None) == -3
     need = lib.pa_decode_workspace_size(ref(good), 3, 4, 1024, 16)
     assert need > 0 and need % 256 == 0
     assert lib.pa_decode_workspace_size(ref(good), 3, 4, 16, 16) == 0

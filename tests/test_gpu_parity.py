@@ -151,12 +151,23 @@ def test_decode_every_step_of_the_growth_workload():
 # ------------------------------------------------------------------ invariants and closed forms
 
 
-def _decode_custom(w, pool_np, tables, lens, q, partition_size=0, max_context_len=None):
+def _decode_custom(w, pool_np, tables, lens, q, partition_size=0, max_context_len=None, keep_cached=False):
     pool = pa.PagedKVPool(to_dev(pool_np, w.dtype))
     mcl = int(np.max(lens)) if max_context_len is None else max_context_len
     out = pa.pa_decode(pool, to_dev(q, w.dtype), i32(tables), i32(lens), scale=float(w.scale),
-                       max_context_len=mcl, partition_size=partition_size)
+                       max_context_len=mcl, partition_size=partition_size, keep_cached=keep_cached)
     return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_cache_policy_flag_does_not_change_results(k):
+    w = make_config(k, small=True)
+    say(f"[cache policy] {w.name}")
+    _, pool_np = oracle_step(w, w.pool, 0)
+    st = w.steps[0]
+    a = _decode_custom(w, pool_np, w.block_tables, st.context_lens, st.q, 64, keep_cached=False)
+    b = _decode_custom(w, pool_np, w.block_tables, st.context_lens, st.q, 64, keep_cached=True)
+    assert a.tobytes() == b.tobytes()
 
 
 @pytest.mark.parametrize("partition_size", [0, 32])
