@@ -65,6 +65,45 @@ def measured_traffic(workload: int, partition_size: int):
     return e.get("hbm_bytes_per_launch")
 
 
+def block_manager_timing(w, steps: int = 32, oracle_steps: int = 4):
+    """Host bookkeeping of one decode step with the native block manager (include/pa_blocks.h):
+    every sequence of the workload appends one token (growth, copy-on-write check, slot), then
+    the batch's block tables are exported.  Timed beside the oracle's Python pool doing the
+    same appends."""
+    import copy
+
+    import paged_kv_cache_121_amd as pa
+    from oracle import alloc
+    lens = w.steps[0].context_lens
+    S, B = len(lens), w.block_size
+    bm = pa.pa_bm_create(w.num_blocks, B, reserve_null_block=True)
+    seqs = np.array([pa.pa_bm_add_sequence(bm) for _ in range(S)], dtype=np.int64)
+    pool = alloc.BlockPool(w.num_blocks, B, reserve_null_block=True)
+    oseqs = [alloc.Sequence() for _ in range(S)]
+    for i, L in enumerate(lens):
+        pa.pa_bm_allocate_prompt(bm, int(seqs[i]), int(L) - 1)
+        alloc.allocate_prompt(pool, oseqs[i], int(L) - 1)
+    width = -(-(int(lens.max()) + steps) // B)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pa.pa_bm_append_tokens(bm, seqs)
+    t_append = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pa.pa_bm_block_tables(bm, seqs, width)
+    t_tables = (time.perf_counter() - t0) / steps
+    pa.pa_bm_destroy(bm)
+    t0 = time.perf_counter()
+    for _ in range(oracle_steps):
+        for s in oseqs:
+            alloc.prepare_write(pool, s, s.num_tokens)
+    t_oracle = (time.perf_counter() - t0) / oracle_steps
+    return {"sequences": S, "append_step_us": round(t_append * 1e6, 1),
+            "append_ns_per_sequence": round(t_append * 1e9 / S, 1),
+            "tables_export_us": round(t_tables * 1e6, 1),
+            "oracle_append_step_us": round(t_oracle * 1e6, 1)}
+
+
 def cpu_baseline(w, n_seqs: int):
     """The float64 oracle on a bounded sample of the same workload, one BLAS thread."""
     from threadpoolctl import threadpool_limits
@@ -211,6 +250,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seqs)
+    host_bm = block_manager_timing(w)
 
     line = {
         "metric": METRIC,
@@ -242,6 +282,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
+        "block_manager": host_bm,
         "sampled_max_abs_err": check,
     }
     print(json.dumps(line), flush=True)

@@ -1,0 +1,120 @@
+/*
+ * pa_blocks.h -- host-side block manager of the paged KV cache (C ABI).
+ *
+ * The bookkeeping around the kernels of pa.h, as the pages describe it:
+ *   [TSS]   "Paging: blocks handed out as tokens arrive" and "Inside vLLM:
+ *           the block pool": a pool of fixed-size blocks, a free queue
+ *           taken from the front, a reference count per allocated block, a
+ *           never-allocated null block 0, and ordered freeing (a block whose
+ *           count reaches zero goes to the back of the queue when its
+ *           contents may be reused, else to the front);
+ *   [HRL]   "What Does PagedAttention Actually Optimize?" section 17
+ *           (ensure_capacity: a sequence grows by one block when a write
+ *           reaches past its table) and section 18 (blocks return on finish);
+ *   [AINEW] copy-on-write passage, [SALIV] "Advanced Memory Sharing and
+ *           Copy-on-Write", [VIBE] vLLM procedure step 6: a write into a
+ *           block with more than one reference first clones it to a fresh
+ *           block, drops one reference of the original and repoints only
+ *           the writer's table;
+ *   [TSS]   "Finding a token": slot = block * block_size + offset.
+ *
+ * Everything here runs on the host and touches no device memory: it emits
+ * the slots, copy-on-write pairs and block tables that pa.h's kernels take.
+ * A manager is not thread-safe; use one per scheduling thread.  All
+ * pointers are host pointers.  Errors return a negative status (pa.h's
+ * pa_status values plus PA_ERR_OUT_OF_BLOCKS) and leave the manager exactly
+ * as it was before the call.
+ */
+#ifndef PA_BLOCKS_H
+#define PA_BLOCKS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* No free block is left for the request ([VIBE] step 7: where vLLM preempts). */
+#define PA_ERR_OUT_OF_BLOCKS (-5)
+/* An unknown sequence id. */
+#define PA_ERR_NO_SEQUENCE (-6)
+
+typedef struct pa_block_manager pa_block_manager;
+
+/*
+ * Create a manager of num_blocks blocks of block_size tokens.  With
+ * reserve_null_block != 0, block 0 is never handed out.  free_order (may be
+ * NULL: ascending ids) lists the initial free queue front to back; it must
+ * hold distinct ids in [0, num_blocks); ids it omits start out unavailable
+ * (held by something outside this manager).  The null block is dropped from
+ * it.  *out receives the manager; release it with pa_bm_destroy.
+ */
+int pa_bm_create(int64_t num_blocks, int32_t block_size, int32_t reserve_null_block,
+                 const int32_t *free_order, int64_t free_order_len, pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+
+/* A new, empty sequence; *seq_out receives its id (ids are never reused). */
+int pa_bm_add_sequence(pa_block_manager *bm, int64_t *seq_out);
+
+/*
+ * A new sequence whose table points at the first num_shared_blocks blocks of
+ * `parent` (all of them when negative), each gaining one reference; its
+ * token count is min(parent's, num_shared_blocks * block_size).
+ */
+int pa_bm_fork(pa_block_manager *bm, int64_t parent, int32_t num_shared_blocks, int64_t *child_out);
+
+/*
+ * Prefill allocation: grow `seq` to ceil(num_tokens / block_size) blocks
+ * ([VIBE] step 3) and set its token count to max(count, num_tokens).
+ */
+int pa_bm_allocate_prompt(pa_block_manager *bm, int64_t seq, int32_t num_tokens);
+
+/*
+ * Make position `position` of `seq` writable: grow the table to cover it,
+ * then copy-on-write if the block holding it has more than one reference.
+ * *slot receives the token's slot; *cow_src / *cow_dst receive the block
+ * pair to copy before the write, or -1 when none is needed.  The sequence's
+ * token count becomes max(count, position + 1).
+ */
+int pa_bm_prepare_write(pa_block_manager *bm, int64_t seq, int32_t position, int64_t *slot, int32_t *cow_src,
+                        int32_t *cow_dst);
+
+/*
+ * One decode step for n sequences: each appends one token at its current
+ * token count (growth, copy-on-write, slot), in array order.  slots_out
+ * [n]; the copy-on-write pairs go to cow_src_out / cow_dst_out (room for n
+ * pairs each) and their count to *num_cow_out.  All or nothing: when the
+ * free queue cannot cover every new and copied block, nothing changes and
+ * PA_ERR_OUT_OF_BLOCKS is returned.  A sequence listed twice is invalid.
+ */
+int pa_bm_append_tokens(pa_block_manager *bm, const int64_t *seqs, int32_t n, int64_t *slots_out,
+                        int32_t *cow_src_out, int32_t *cow_dst_out, int32_t *num_cow_out);
+
+/*
+ * Release every block of `seq` and forget it ([HRL] section 18 step 8).
+ * Blocks reaching zero references go to the back of the free queue when
+ * reusable != 0, else to the front.
+ */
+int pa_bm_free_sequence(pa_block_manager *bm, int64_t seq, int32_t reusable);
+
+/*
+ * Block tables of n sequences as int32 [n][max_blocks_per_seq] (entries past
+ * a sequence's blocks are pad_value) plus their token counts lens_out[n].
+ * A sequence with more than max_blocks_per_seq blocks is an error.
+ */
+int pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t max_blocks_per_seq,
+                       int32_t pad_value, int32_t *tables_out, int32_t *lens_out);
+
+/* Queries: counts, one block's references, one sequence's shape, the queue. */
+int64_t pa_bm_num_free(const pa_block_manager *bm);
+int64_t pa_bm_num_sequences(const pa_block_manager *bm);
+int32_t pa_bm_refcount(const pa_block_manager *bm, int32_t block);
+int pa_bm_sequence_info(const pa_block_manager *bm, int64_t seq, int32_t *num_tokens, int32_t *num_blocks);
+/* Free queue front to back into out[cap]; returns the queue length (may exceed cap). */
+int64_t pa_bm_free_queue(const pa_block_manager *bm, int32_t *out, int64_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_BLOCKS_H */

@@ -8,6 +8,10 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 * ``pa_block_copy(pool, src_blocks, dst_blocks)``
 * ``pa_decode(pool, q, block_tables, context_lens, ...) -> out``
 * ``pa_decode_workspace_size(...)``, ``pa_decode_partition_size(...)``
+* the host block manager of ``include/pa_blocks.h``: ``pa_bm_create``,
+  ``pa_bm_add_sequence``, ``pa_bm_fork``, ``pa_bm_allocate_prompt``,
+  ``pa_bm_prepare_write``, ``pa_bm_append_tokens``, ``pa_bm_free_sequence``,
+  ``pa_bm_block_tables`` and the queries (host numpy arrays in and out)
 
 Tensors live on a ROCm device (torch provides memory and the current
 stream).  There is no fallback: if libpa.so is missing or the device is not
@@ -22,11 +26,26 @@ import os
 import threading
 
 __all__ = [
+    "OutOfBlocks",
     "PaError",
     "PagedKVPool",
     "library_path",
     "load_library",
     "pa_block_copy",
+    "pa_bm_add_sequence",
+    "pa_bm_allocate_prompt",
+    "pa_bm_append_tokens",
+    "pa_bm_block_tables",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_fork",
+    "pa_bm_free_queue",
+    "pa_bm_free_sequence",
+    "pa_bm_num_free",
+    "pa_bm_num_sequences",
+    "pa_bm_prepare_write",
+    "pa_bm_refcount",
+    "pa_bm_sequence_info",
     "pa_cache_write",
     "pa_decode",
     "pa_decode_partition_size",
@@ -48,6 +67,10 @@ class PaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {pa_status_str(status)} (status {status})")
+
+
+class OutOfBlocks(PaError):
+    """The block manager has no free block for the request (state unchanged)."""
 
 
 class pa_pool(ctypes.Structure):
@@ -74,7 +97,24 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
+    # host block manager (include/pa_blocks.h)
+    "pa_bm_create": (_I32, [_I64, _I32, _I32, _VP, _I64, ctypes.POINTER(_VP)]),
+    "pa_bm_destroy": (None, [_VP]),
+    "pa_bm_add_sequence": (_I32, [_VP, ctypes.POINTER(_I64)]),
+    "pa_bm_fork": (_I32, [_VP, _I64, _I32, ctypes.POINTER(_I64)]),
+    "pa_bm_allocate_prompt": (_I32, [_VP, _I64, _I32]),
+    "pa_bm_prepare_write": (_I32, [_VP, _I64, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32),
+                                   ctypes.POINTER(_I32)]),
+    "pa_bm_append_tokens": (_I32, [_VP, _VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32)]),
+    "pa_bm_free_sequence": (_I32, [_VP, _I64, _I32]),
+    "pa_bm_block_tables": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "pa_bm_num_free": (_I64, [_VP]),
+    "pa_bm_num_sequences": (_I64, [_VP]),
+    "pa_bm_refcount": (_I32, [_VP, _I32]),
+    "pa_bm_sequence_info": (_I32, [_VP, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "pa_bm_free_queue": (_I64, [_VP, _VP, _I64]),
 }
+PA_ERR_OUT_OF_BLOCKS = -5
 
 
 def load_library(path: str | None = None):
@@ -108,6 +148,8 @@ def _torch():
 
 
 def _check(status: int, where: str) -> None:
+    if status == PA_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocks(status, where)
     if status != 0:
         raise PaError(status, where)
 
@@ -283,3 +325,122 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
                          PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM, _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
                          _stream(q)), "pa_decode")
     return out
+
+
+# ---------------------------------------------------------------------------
+# host block manager (include/pa_blocks.h): handles are opaque pointers,
+# arrays are host numpy arrays
+# ---------------------------------------------------------------------------
+
+
+def _np():
+    import numpy as np
+    return np
+
+
+def _host(a, dtype):
+    np = _np()
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def pa_bm_create(num_blocks: int, block_size: int, reserve_null_block: bool = False, free_order=None):
+    """A block manager; release it with ``pa_bm_destroy``."""
+    lib = load_library()
+    out = ctypes.c_void_p()
+    if free_order is None:
+        st = lib.pa_bm_create(num_blocks, block_size, int(reserve_null_block), None, 0, ctypes.byref(out))
+    else:
+        fo = _host(free_order, "int32")
+        st = lib.pa_bm_create(num_blocks, block_size, int(reserve_null_block), fo.ctypes.data, len(fo),
+                              ctypes.byref(out))
+    _check(st, "pa_bm_create")
+    return out
+
+
+def pa_bm_destroy(bm) -> None:
+    load_library().pa_bm_destroy(bm)
+
+
+def pa_bm_add_sequence(bm) -> int:
+    out = ctypes.c_int64()
+    _check(load_library().pa_bm_add_sequence(bm, ctypes.byref(out)), "pa_bm_add_sequence")
+    return out.value
+
+
+def pa_bm_fork(bm, parent: int, num_shared_blocks: int = -1) -> int:
+    out = ctypes.c_int64()
+    _check(load_library().pa_bm_fork(bm, parent, num_shared_blocks, ctypes.byref(out)), "pa_bm_fork")
+    return out.value
+
+
+def pa_bm_allocate_prompt(bm, seq: int, num_tokens: int) -> None:
+    _check(load_library().pa_bm_allocate_prompt(bm, seq, num_tokens), "pa_bm_allocate_prompt")
+
+
+def pa_bm_prepare_write(bm, seq: int, position: int):
+    """(slot, (cow_src, cow_dst) or None) for writing ``position`` of ``seq``."""
+    slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().pa_bm_prepare_write(bm, seq, position, ctypes.byref(slot), ctypes.byref(src),
+                                              ctypes.byref(dst)), "pa_bm_prepare_write")
+    return slot.value, ((src.value, dst.value) if src.value >= 0 else None)
+
+
+def pa_bm_append_tokens(bm, seqs):
+    """One token per sequence: (slots int64[n], cow_src int32[k], cow_dst int32[k])."""
+    np = _np()
+    seqs = _host(seqs, "int64")
+    n = len(seqs)
+    slots = np.empty(n, dtype=np.int64)
+    src = np.empty(max(n, 1), dtype=np.int32)
+    dst = np.empty(max(n, 1), dtype=np.int32)
+    k = ctypes.c_int32()
+    _check(load_library().pa_bm_append_tokens(bm, seqs.ctypes.data, n, slots.ctypes.data, src.ctypes.data,
+                                              dst.ctypes.data, ctypes.byref(k)), "pa_bm_append_tokens")
+    return slots, src[:k.value].copy(), dst[:k.value].copy()
+
+
+def pa_bm_free_sequence(bm, seq: int, reusable: bool = False) -> None:
+    _check(load_library().pa_bm_free_sequence(bm, seq, int(reusable)), "pa_bm_free_sequence")
+
+
+def pa_bm_block_tables(bm, seqs, max_blocks_per_seq: int, pad_value: int = 0):
+    """(tables int32[n][max_blocks_per_seq], token counts int32[n])."""
+    np = _np()
+    seqs = _host(seqs, "int64")
+    n = len(seqs)
+    tables = np.empty((n, max_blocks_per_seq), dtype=np.int32)
+    lens = np.empty(n, dtype=np.int32)
+    _check(load_library().pa_bm_block_tables(bm, seqs.ctypes.data, n, max_blocks_per_seq, pad_value,
+                                             tables.ctypes.data, lens.ctypes.data), "pa_bm_block_tables")
+    return tables, lens
+
+
+def pa_bm_num_free(bm) -> int:
+    return int(load_library().pa_bm_num_free(bm))
+
+
+def pa_bm_num_sequences(bm) -> int:
+    return int(load_library().pa_bm_num_sequences(bm))
+
+
+def pa_bm_refcount(bm, block: int) -> int:
+    r = load_library().pa_bm_refcount(bm, block)
+    _check(min(r, 0), "pa_bm_refcount")
+    return int(r)
+
+
+def pa_bm_sequence_info(bm, seq: int):
+    """(token count, block count) of ``seq``."""
+    t, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().pa_bm_sequence_info(bm, seq, ctypes.byref(t), ctypes.byref(b)), "pa_bm_sequence_info")
+    return t.value, b.value
+
+
+def pa_bm_free_queue(bm):
+    """The free queue, front to back (int32 array)."""
+    np = _np()
+    lib = load_library()
+    n = int(lib.pa_bm_free_queue(bm, None, 0))
+    out = np.empty(max(n, 1), dtype=np.int32)
+    lib.pa_bm_free_queue(bm, out.ctypes.data, n)
+    return out[:n].copy()

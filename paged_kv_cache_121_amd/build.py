@@ -23,7 +23,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip"]
+SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip"]  # HIP: device and host code
+HOST_SOURCES = ["block_manager.cpp"]                      # host-only C++ (g++)
+ROCM_INCLUDE = "/opt/rocm/include"
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -46,7 +48,12 @@ def _hipcc() -> str:
 
 def _compile(src: str, hipcc: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cxx = shutil.which("g++") or "g++"
+        cmd = [cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", f"-I{CSRC}",
+               f"-I{ROCM_INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -58,8 +65,9 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra_flags or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc, extra), SOURCES))
+    sources = SOURCES + HOST_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(sources), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, hipcc, extra), sources))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

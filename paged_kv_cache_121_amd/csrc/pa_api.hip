@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstring>
 
+#include "pa_blocks.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -93,6 +94,8 @@ const char *pa_status_str(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failure";
+    case PA_ERR_OUT_OF_BLOCKS: return "out of free blocks";
+    case PA_ERR_NO_SEQUENCE: return "unknown sequence id";
     default: return "unknown status";
   }
 }
