@@ -175,6 +175,34 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
               int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
               int32_t flags, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Prefill or chunked prefill: many query rows per sequence, causal
+ * ([HRL] section 9, prefill computes a prompt's tokens together; [TSS]
+ * "Next", chunked prefill takes a prompt a chunk at a time; [HRL] section 8
+ * for the formula).  The K/V of every position must already be in the pool
+ * (pa_cache_write).
+ *   q               : [total_tokens][num_q_heads][head_dim], bf16.
+ *   out             : float32 [total_tokens][num_q_heads][head_dim].
+ *   query_start_loc : int32 [num_seqs + 1]; sequence s owns rows
+ *                     query_start_loc[s] .. query_start_loc[s+1]-1, which are
+ *                     its last n_s positions: row i is at position
+ *                     context_lens[s] - n_s + i and attends over cached
+ *                     positions 0 .. that position.
+ *   context_lens    : int32 [num_seqs], cached tokens (this chunk included).
+ *   block_tables    : int32 [num_seqs][max_blocks_per_seq].
+ *   max_query_len   : host-known upper bound of n_s.
+ * bf16 pools only (the contraction runs on the bf16 matrix cores); head_dim
+ * 64 or 128; block size 16 or 32; group size 1, 2, 4 or 8.  Rows of a
+ * sequence whose bounds are inconsistent (n_s < 0, n_s > context length,
+ * n_s > max_query_len, rows outside [0, total_tokens), context beyond the
+ * table row) are NaN where they lie inside the output, and so are the rows
+ * of a 64-row tile that read a table id outside [0, num_blocks).
+ */
+int pa_prefill(const pa_pool *pool, const void *q, float *out, const int32_t *query_start_loc,
+               const int32_t *context_lens, const int32_t *block_tables, int32_t max_blocks_per_seq,
+               int32_t num_seqs, int32_t num_q_heads, int32_t total_tokens, int32_t max_query_len, float scale,
+               hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *pa_status_str(int status);
 

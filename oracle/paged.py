@@ -247,3 +247,43 @@ def decode_one_ref(pool: np.ndarray, q: np.ndarray, block_tables, context_lens, 
         return np.zeros(pool.shape[4], dtype=np.float64)
     keys, values = gather_ref(pool, block_tables[seq], length, q_head // group)
     return attention_ref(to_f64(q[seq, q_head]), keys, values, scale)
+
+
+def prefill_ref(pool: np.ndarray, q: np.ndarray, query_start_loc, context_lens, block_tables,
+                scale: float) -> np.ndarray:
+    """Prefill (or chunked prefill) attention of many queries per sequence, causal.
+
+    [HRL] §9 "How PagedAttention Appears in Prefill and Decode": prefill runs
+    the prompt's tokens together and fills their K/V into the blocks;
+    [TSS] "Next": chunked prefill processes a prompt a piece at a time.
+    Sequence ``s`` owns query rows ``query_start_loc[s] .. query_start_loc[s+1]-1``;
+    they are its last ``n_s`` positions, so row ``i`` sits at position
+    ``p = context_lens[s] - n_s + i`` and attends, as ordinary causal attention
+    does, over cached positions ``0 .. p`` found through the block table
+    ([HRL] §8 formula; §14 table walk).  ``q`` is ``[T][Hq][D]`` in the pool's
+    storage dtype; the result is float64 ``[T][Hq][D]``.
+    """
+    num_kv_heads = pool.shape[2]
+    head_dim = pool.shape[4]
+    q = np.asarray(q)
+    total, num_q_heads, qd = q.shape
+    assert qd == head_dim and num_q_heads % num_kv_heads == 0
+    group = num_q_heads // num_kv_heads
+    q64 = to_f64(q)
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    starts = np.asarray(query_start_loc, dtype=np.int64)
+    for s in range(len(starts) - 1):
+        n = int(starts[s + 1] - starts[s])
+        ctx = int(context_lens[s])
+        if n == 0:
+            continue
+        assert 0 < n <= ctx
+        for h in range(num_kv_heads):
+            keys, values = gather_ref(pool, block_tables[s], ctx, h)
+            for i in range(n):
+                pos = ctx - n + i
+                row = int(starts[s]) + i
+                for g in range(group):
+                    hq = h * group + g
+                    out[row, hq] = attention_ref(q64[row, hq], keys[:pos + 1], values[:pos + 1], scale)
+    return out

@@ -8,6 +8,7 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 * ``pa_block_copy(pool, src_blocks, dst_blocks)``
 * ``pa_decode(pool, q, block_tables, context_lens, ...) -> out``
 * ``pa_decode_workspace_size(...)``, ``pa_decode_partition_size(...)``
+* ``pa_prefill(pool, q, query_start_loc, context_lens, block_tables, ...) -> out``
 * the host block manager of ``include/pa_blocks.h``: ``pa_bm_create``,
   ``pa_bm_add_sequence``, ``pa_bm_fork``, ``pa_bm_allocate_prompt``,
   ``pa_bm_prepare_write``, ``pa_bm_append_tokens``, ``pa_bm_free_sequence``,
@@ -50,6 +51,7 @@ __all__ = [
     "pa_decode",
     "pa_decode_partition_size",
     "pa_decode_workspace_size",
+    "pa_prefill",
     "pa_slot_mapping",
     "pa_status_str",
 ]
@@ -97,6 +99,7 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
+    "pa_prefill": (_I32, [_POOLP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     # host block manager (include/pa_blocks.h)
     "pa_bm_create": (_I32, [_I64, _I32, _I32, _VP, _I64, ctypes.POINTER(_VP)]),
     "pa_bm_destroy": (None, [_VP]),
@@ -324,6 +327,37 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
                          _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size),
                          PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM, _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
                          _stream(q)), "pa_decode")
+    return out
+
+
+def pa_prefill(pool: PagedKVPool, q, query_start_loc, context_lens, block_tables, scale: float | None = None,
+               max_query_len: int | None = None, out=None):
+    """Causal (chunked) prefill attention over the paged cache; returns float32 ``[T][Hq][D]``.
+
+    ``max_query_len`` defaults to the number of query rows (a bound known on
+    the host without reading ``query_start_loc`` back).
+    """
+    torch = _torch()
+    dev = pool.device
+    _dev_tensor(q, "q", pool.data.dtype, 3, dev)
+    T, Hq, D = (int(x) for x in q.shape)
+    _need(D == pool.head_dim, "q head_dim must match the pool")
+    _dev_tensor(query_start_loc, "query_start_loc", torch.int32, 1, dev)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1, dev)
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2, dev)
+    S = int(context_lens.shape[0])
+    _need(query_start_loc.shape[0] == S + 1 and block_tables.shape[0] == S, "one table row and length per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_query_len is None:
+        max_query_len = T
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    _dev_tensor(out, "out", torch.float32, 3, dev)
+    _need(tuple(out.shape) == (T, Hq, D), "out must be [T][Hq][D]")
+    _check(load_library().pa_prefill(pool.desc, _ptr(q), _ptr(out), _ptr(query_start_loc), _ptr(context_lens),
+                                      _ptr(block_tables), int(block_tables.shape[1]), S, Hq, T, int(max_query_len),
+                                      float(scale), _stream(q)), "pa_prefill")
     return out
 
 

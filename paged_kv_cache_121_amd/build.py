@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip"]  # HIP: device and host code
+SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]  # HIP: device and host code
 HOST_SOURCES = ["block_manager.cpp"]                      # host-only C++ (g++)
 ROCM_INCLUDE = "/opt/rocm/include"
 

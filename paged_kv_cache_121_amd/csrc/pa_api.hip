@@ -205,4 +205,38 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
   return status_of(launch_decode(a, stream));
 }
 
+int pa_prefill(const pa_pool *pool, const void *q, float *out, const int32_t *query_start_loc,
+               const int32_t *context_lens, const int32_t *block_tables, int32_t max_blocks_per_seq,
+               int32_t num_seqs, int32_t num_q_heads, int32_t total_tokens, int32_t max_query_len, float scale,
+               hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || total_tokens < 0 || max_query_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % d.num_kv_heads != 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * d.block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!prefill_supported(d.dtype, d.head_dim, d.block_size, num_q_heads / d.num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0 || total_tokens == 0) return PA_OK;
+  if (q == nullptr || out == nullptr || query_start_loc == nullptr || context_lens == nullptr ||
+      block_tables == nullptr)
+    return PA_ERR_INVALID_ARG;
+  PrefillArgs a{};
+  a.pool = d;
+  a.q = q;
+  a.out = out;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = context_lens;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.total_tokens = total_tokens;
+  a.max_query_len = max_query_len;
+  a.scale = scale;
+  return status_of(launch_prefill(a, stream));
+}
+
 }  // extern "C"

@@ -44,6 +44,21 @@ struct DecodeArgs {
   float *ws_ml;          // [S][Hq][P][2] running max (log2 units) and sum
 };
 
+struct PrefillArgs {
+  PoolDesc pool;
+  const void *q;
+  float *out;
+  const int32_t *query_start_loc;
+  const int32_t *context_lens;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int total_tokens;
+  int max_query_len;
+  float scale;
+};
+
 // Workspace layout of one decode call; every region 256-byte aligned.
 struct WorkspaceLayout {
   size_t o_off, ml_off, total;
@@ -61,5 +76,7 @@ hipError_t launch_block_copy(const PoolDesc &pool, const int32_t *src, const int
 // Returns hipErrorInvalidValue when no kernel is built for the shape.
 hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int block_size, int group);
+hipError_t launch_prefill(const PrefillArgs &args, hipStream_t stream);
+bool prefill_supported(int dtype, int head_dim, int block_size, int group);
 
 }  // namespace pa

@@ -69,6 +69,12 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, float("nan"), 48, 0, 0, None, 0, None) == -1
     assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 0, 2, None, 0, None) == -1  # unknown flag
     assert lib.pa_decode(ref(good), 1, 1, 1, 64, 1, 3, 4, 0.1, 1024, 16, 0, None, 0, None) == -3
+    # prefill: bf16 pools only (the contraction runs on bf16 matrix cores); zero work is a no-op
+    assert lib.pa_prefill(ref(good), 1, 1, 1, 1, 1, 4, 3, 4, 10, 10, 0.1, None) == -2
+    bf = pa.pa_pool(0x1000, 16, 4, 16, 64, pa.PA_BF16)
+    assert lib.pa_prefill(ref(bf), None, None, None, None, None, 4, 0, 4, 0, 0, 0.1, None) == 0
+    assert lib.pa_prefill(ref(bf), 1, 1, 1, 1, 1, 4, 3, 12, 10, 10, 0.1, None) == -2  # group 3
+    assert lib.pa_prefill(ref(bf), 1, 1, 1, 1, 1, 4, 3, 4, -1, 10, 0.1, None) == -1
     need = lib.pa_decode_workspace_size(ref(good), 3, 4, 1024, 16)
     assert need > 0 and need % 256 == 0
     assert lib.pa_decode_workspace_size(ref(good), 3, 4, 16, 16) == 0

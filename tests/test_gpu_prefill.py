@@ -1,0 +1,146 @@
+"""GPU parity of the MFMA prefill kernel (pa_prefill) against the float64 oracle.
+
+Each case first writes the chunk's K/V through pa_slot_mapping + pa_cache_write
+(the prefill write path), then runs pa_prefill; the oracle replays the same
+write with its own routines and computes causal attention row by row.
+Bar: max-abs error 2e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_121_amd as pa
+from oracle import paged
+from workloads import make_prefill, make_prefill_custom
+
+from _gpu_util import device_pool, i32, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+def gpu_prefill(w, pool=None, max_query_len=None):
+    pool = pool or device_pool(w)
+    tables = i32(w.block_tables)
+    slots = pa.pa_slot_mapping(pool, tables, i32(w.write_seq), i32(w.write_pos))
+    pa.pa_cache_write(pool, to_dev(w.k_new, w.dtype), to_dev(w.v_new, w.dtype), slots)
+    n = np.diff(w.query_start_loc)
+    out = pa.pa_prefill(pool, to_dev(w.q, w.dtype), i32(w.query_start_loc), i32(w.context_lens), tables,
+                        scale=float(w.scale), max_query_len=int(n.max()) if max_query_len is None else max_query_len)
+    torch.cuda.synchronize()
+    return pool, out.cpu().numpy()
+
+
+def oracle_pool(w):
+    slots = paged.slot_mapping_ref(w.block_tables, w.write_seq, w.write_pos, w.block_size)
+    return paged.cache_write_ref(w.pool, w.k_new, w.v_new, slots)
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_prefill_small_workloads_match_oracle(k):
+    w = make_prefill(k, small=True)
+    say(f"[prefill] {w.name}")
+    pool, got = gpu_prefill(w)
+    pool_np = oracle_pool(w)
+    assert to_host(pool.data).tobytes() == pool_np.tobytes()  # the prefill write, bit for bit
+    want = paged.prefill_ref(pool_np, w.q, w.query_start_loc, w.context_lens, w.block_tables, float(w.scale))
+    err = np.abs(got.astype(np.float64) - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
+
+
+@pytest.mark.parametrize("group,head_dim,block_size", [
+    (1, 128, 16), (2, 128, 32), (4, 64, 16), (8, 128, 32), (8, 64, 16), (4, 128, 32),
+])
+def test_prefill_shapes_chunks_and_ragged_tails(group, head_dim, block_size):
+    hkv = 2
+    ctx = [1, 63, 64, 65, 150, 200]
+    chunk = [1, 63, 10, 65, 33, 129]   # whole prompts, chunks, a one-row chunk
+    w = make_prefill_custom(name="prefill-shapes", seed=7 + group, dtype="bf16", num_blocks=128,
+                            num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=head_dim,
+                            block_size=block_size, context_lens=ctx, chunk_lens=chunk)
+    say(f"[prefill shapes] G={group} D={head_dim} B={block_size}")
+    _, got = gpu_prefill(w)
+    want = paged.prefill_ref(oracle_pool(w), w.q, w.query_start_loc, w.context_lens, w.block_tables,
+                             float(w.scale))
+    err = np.abs(got.astype(np.float64) - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
+
+
+def test_prefill_single_row_chunks_agree_with_decode():
+    w = make_prefill_custom(name="prefill-vs-decode", seed=31, dtype="bf16", num_blocks=96, num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16, context_lens=[17, 300, 64, 5],
+                            chunk_lens=[1, 1, 1, 1])
+    say("[prefill vs decode] one-row chunks")
+    pool, got = gpu_prefill(w)
+    dec = pa.pa_decode(pool, to_dev(w.q, w.dtype), i32(w.block_tables), i32(w.context_lens), scale=float(w.scale),
+                       max_context_len=300).cpu().numpy()
+    assert np.abs(got - dec).max() <= 1e-5
+
+
+def test_prefill_padding_poison_is_never_read():
+    w = make_prefill_custom(name="prefill-poison", seed=41, dtype="bf16", num_blocks=64, num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, block_size=16, context_lens=[45, 70],
+                            chunk_lens=[45, 20])
+    say("[prefill poison]")
+    pool_np = oracle_pool(w)
+    poisoned = pool_np.copy()
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        for t in range(L, -(-L // 16) * 16):
+            b, o = paged.translate(w.block_tables[s], t, 16)
+            poisoned[b, :, :, o, :] = 0x7FC0
+    pool = pa.PagedKVPool(to_dev(poisoned, "bf16"))
+    out = pa.pa_prefill(pool, to_dev(w.q, "bf16"), i32(w.query_start_loc), i32(w.context_lens),
+                        i32(w.block_tables), scale=float(w.scale), max_query_len=45).cpu().numpy()
+    want = paged.prefill_ref(pool_np, w.q, w.query_start_loc, w.context_lens, w.block_tables, float(w.scale))
+    assert np.isfinite(out).all() and np.abs(out - want).max() <= ATOL
+
+
+def test_prefill_inconsistent_rows_are_nan_and_others_exact():
+    w = make_prefill_custom(name="prefill-edge", seed=51, dtype="bf16", num_blocks=64, num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, block_size=16, context_lens=[40, 30, 50],
+                            chunk_lens=[10, 10, 10])
+    say("[prefill edge rows]")
+    pool_np = oracle_pool(w)
+    pool = pa.PagedKVPool(to_dev(pool_np, "bf16"))
+    lens = w.context_lens.copy()
+    lens[1] = 5                      # fewer cached tokens than query rows: inconsistent
+    tables = w.block_tables.copy()
+    out = pa.pa_prefill(pool, to_dev(w.q, "bf16"), i32(w.query_start_loc), i32(lens), i32(tables),
+                        scale=float(w.scale), max_query_len=10).cpu().numpy()
+    assert np.isnan(out[10:20]).all()
+    good = np.r_[0:10, 20:30]
+    want = paged.prefill_ref(pool_np, w.q, w.query_start_loc, w.context_lens, w.block_tables, float(w.scale))
+    assert np.abs(out[good] - want[good]).max() <= ATOL
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_prefill_fullsize_sampled_rows(k):
+    w = make_prefill(k)
+    say(f"[prefill fullsize] {w.name}: T={w.total_tokens} flops={w.attention_flops() / 1e9:.1f} GFLOP")
+    pool, got = gpu_prefill(w)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(60 + k)
+    errs = []
+    for s in rng.choice(w.num_seqs, size=2, replace=False):
+        # the oracle on this sequence alone: its blocks, its written chunk, a few of its rows
+        n = int(w.query_start_loc[s + 1] - w.query_start_loc[s])
+        ctx = int(w.context_lens[s])
+        nb = -(-ctx // w.block_size)
+        row = w.block_tables[s, :nb]
+        small = w.pool[row].copy()
+        tbl = np.arange(nb, dtype=np.int32)[None, :]
+        sel = slice(int(w.query_start_loc[s]), int(w.query_start_loc[s + 1]))
+        slots = paged.slot_mapping_ref(tbl, np.zeros(n, dtype=np.int32), w.write_pos[sel], w.block_size)
+        small = paged.cache_write_ref(small, w.k_new[sel], w.v_new[sel], slots)
+        pick = sorted(set([0, n - 1] + list(rng.choice(n, size=3))))
+        qs = w.q[sel][pick]
+        for j, i in enumerate(pick):
+            want = paged.prefill_ref(small, qs[j:j + 1], [0, 1], [ctx - n + i + 1], tbl, float(w.scale))
+            errs.append(np.abs(got[int(w.query_start_loc[s]) + i].astype(np.float64) - want[0]).max())
+    say(f"    {len(errs)} sampled rows, max abs err {max(errs):.3e}")
+    assert max(errs) <= ATOL

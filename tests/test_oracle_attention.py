@@ -240,3 +240,57 @@ def test_block_copy_copies_whole_blocks_only():
     assert np.array_equal(out[3], pool[1]) and np.array_equal(out[0], pool[6])
     for b in (1, 2, 4, 5, 6, 7):
         assert np.array_equal(out[b], pool[b])
+
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def test_prefill_single_query_rows_equal_decode():
+    """A chunk of one query per sequence is a decode step (same positions, same keys)."""
+    rng = np.random.default_rng(14)
+    lengths = [9, 14, 3]
+    pool, tables, q = _random_case(rng, lengths)
+    dec = paged.decode_ref(pool, q, tables, lengths, 0.4)
+    pre = paged.prefill_ref(pool, q, [0, 1, 2, 3], lengths, tables, 0.4)
+    assert np.array_equal(dec, pre)
+
+
+def test_prefill_matches_torch_causal_sdpa_float64():
+    """Full prefill (queries = whole context) is textbook causal attention."""
+    rng = np.random.default_rng(15)
+    lengths = [13, 7]
+    hq, hkv, D = 4, 2, 8
+    pool, tables, contig = build_paged(rng, lengths, hkv, D, 4, 12, "f32", list(rng.permutation(12)))
+    q = rng.standard_normal((sum(lengths), hq, D)).astype(np.float32)
+    out = paged.prefill_ref(pool, q, [0, 13, 20], lengths, tables, 0.3)
+    start = 0
+    for s, L in enumerate(lengths):
+        kv = paged.to_f64(contig[s])  # [L][2][Hkv][D]
+        for h in range(hq):
+            k = torch.from_numpy(kv[:, 0, h // 2])[None, None]
+            v = torch.from_numpy(kv[:, 1, h // 2])[None, None]
+            qq = torch.from_numpy(q[start:start + L, h].astype(np.float64))[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qq, k, v, is_causal=True, scale=0.3)[0, 0]
+            np.testing.assert_allclose(out[start:start + L, h], ref.numpy(), rtol=0, atol=1e-13)
+        start += L
+
+
+def test_chunked_prefill_matches_brute_force():
+    """A chunk appended to a cached context: row i sees positions 0 .. ctx - n + i."""
+    rng = np.random.default_rng(16)
+    lengths = [11, 6]
+    chunk = [4, 6]
+    hq, hkv, D = 2, 1, 8
+    pool, tables, contig = build_paged(rng, lengths, hkv, D, 4, 8, "f32", list(rng.permutation(8)))
+    q = rng.standard_normal((sum(chunk), hq, D)).astype(np.float32)
+    out = paged.prefill_ref(pool, q, [0, 4, 10], lengths, tables, 0.5)
+    row = 0
+    for s, L in enumerate(lengths):
+        kv = paged.to_f64(contig[s])
+        for i in range(chunk[s]):
+            pos = L - chunk[s] + i
+            for h in range(hq):
+                bf = brute_force_attention(q[row, h].astype(np.float64), kv[:pos + 1, 0, 0], kv[:pos + 1, 1, 0], 0.5)
+                np.testing.assert_allclose(out[row, h], bf, rtol=0, atol=1e-12)
+            row += 1

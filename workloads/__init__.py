@@ -10,6 +10,10 @@ oracle and in the kernels, independently.
 
 from .configs import (  # noqa: F401
     CONFIG_NAMES,
+    PREFILL_NAMES,
+    PrefillWorkload,
+    make_prefill,
+    make_prefill_custom,
     Step,
     Workload,
     make_config,

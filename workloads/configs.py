@@ -289,3 +289,127 @@ def make_config(k: int, small: bool = False) -> Workload:
                            dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
                            block_size=16, lengths=lens, num_steps=steps)
     raise ValueError(f"no workload {k}")
+
+
+# ---------------------------------------------------------------------------
+# prefill workloads
+# ---------------------------------------------------------------------------
+
+PREFILL_NAMES = {
+    1: "prefill: 4 prompts x 4,100 tokens (whole prompt at once), Qwen3-8B layer, B16, bf16",
+    2: "chunked prefill: 16 requests, a 4,000-token prefix shared and cached, 100-token private chunk each, "
+       "Qwen3-8B layer, B16, bf16",
+}
+
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    dtype: str
+    num_blocks: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: np.float32
+    pool: np.ndarray            # positions before each chunk are resident
+    block_tables: np.ndarray    # int32 [S][max_blocks]
+    context_lens: np.ndarray    # int32 [S], chunk included
+    query_start_loc: np.ndarray  # int32 [S+1]
+    q: np.ndarray               # [T][Hq][D]
+    k_new: np.ndarray           # [T][Hkv][D]: the chunk's K, written by the cache write first
+    v_new: np.ndarray
+    write_seq: np.ndarray       # int32 [T]
+    write_pos: np.ndarray       # int32 [T]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.block_tables.shape[0])
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+    def attention_flops(self) -> int:
+        """QK and PV multiply-adds (2 flops each) of the causal rows: 4*D*Hq per (row, key)."""
+        keys = 0
+        for s in range(self.num_seqs):
+            n = int(self.query_start_loc[s + 1] - self.query_start_loc[s])
+            ctx = int(self.context_lens[s])
+            first = ctx - n + 1  # keys seen by the chunk's first row
+            keys += n * first + n * (n - 1) // 2
+        return 4 * self.head_dim * self.num_q_heads * keys
+
+
+def make_prefill_custom(*, name, seed, dtype, num_blocks, num_q_heads, num_kv_heads, head_dim, block_size,
+                        context_lens, chunk_lens, shared_prefix_tokens=0):
+    """Sequences whose last ``chunk_lens[s]`` positions are this step's queries.
+
+    Positions before the chunk are resident in the pool (drawn here); the
+    chunk's K/V are returned for the cache write.  With
+    ``shared_prefix_tokens`` (whole blocks), every sequence's table starts with
+    the same physical blocks holding one common prefix.
+    """
+    rng = np.random.default_rng(seed)
+    B = block_size
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    n = np.asarray(chunk_lens, dtype=np.int64)
+    assert (n >= 1).all() and (n <= ctx).all()
+    S = len(ctx)
+    free = list(rng.permutation(np.arange(1, num_blocks)))
+    free.reverse()
+
+    def take():
+        return int(free.pop())
+
+    shared = []
+    if shared_prefix_tokens:
+        assert shared_prefix_tokens % B == 0 and (ctx - n >= shared_prefix_tokens).all()
+        shared = [take() for _ in range(shared_prefix_tokens // B)]
+    rows = []
+    for s in range(S):
+        row = list(shared)
+        while len(row) < _blocks_for(ctx[s], B):
+            row.append(take())
+        rows.append(row)
+    tables = _tables_array(rows, 0)
+    pool = _empty_pool(num_blocks, num_kv_heads, B, head_dim, dtype)
+    _fill_blocks(pool, set(b for r in rows for b in r), rng, dtype)
+    T = int(n.sum())
+    qsl = np.zeros(S + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(n)
+    q = _normal(rng, (T, num_q_heads, head_dim), dtype)
+    k_new = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+    v_new = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+    write_seq = np.repeat(np.arange(S, dtype=np.int32), n)
+    write_pos = np.concatenate([np.arange(ctx[s] - n[s], ctx[s]) for s in range(S)]).astype(np.int32)
+    scale = np.float32(1.0) / np.sqrt(np.float32(head_dim))
+    return PrefillWorkload(name=name, dtype=dtype, num_blocks=num_blocks, num_q_heads=num_q_heads,
+                           num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, scale=np.float32(scale),
+                           pool=pool, block_tables=tables, context_lens=ctx.astype(np.int32), query_start_loc=qsl,
+                           q=q, k_new=k_new, v_new=v_new, write_seq=write_seq, write_pos=write_pos,
+                           meta={"shared_prefix_tokens": shared_prefix_tokens})
+
+
+def make_prefill(k: int, small: bool = False) -> PrefillWorkload:
+    """Prefill workload ``k`` (1-2); ``small`` keeps the structure at oracle-friendly sizes."""
+    seed = 200 + k + (100 if small else 0)
+    if k == 1:
+        if small:
+            lens, n_blocks = [130, 77, 64, 1], 64
+        else:
+            lens, n_blocks = [4100] * 4, 38348
+        return make_prefill_custom(name="prefill-4x4100" + ("-small" if small else ""), seed=seed, dtype="bf16",
+                                   num_blocks=n_blocks, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                   block_size=16, context_lens=lens, chunk_lens=lens)
+    if k == 2:
+        if small:
+            S, prefix, chunk, n_blocks = 3, 96, 37, 64
+        else:
+            S, prefix, chunk, n_blocks = 16, 4000, 100, 38348
+        return make_prefill_custom(name="chunked-prefill-shared-prefix" + ("-small" if small else ""), seed=seed,
+                                   dtype="bf16", num_blocks=n_blocks, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                   block_size=16, context_lens=[prefix + chunk] * S, chunk_lens=[chunk] * S,
+                                   shared_prefix_tokens=prefix)
+    raise ValueError(f"no prefill workload {k}")
