@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the oracle's timed sample")
     ap.add_argument("--skip-check", action="store_true")
+    ap.add_argument("--prefill", type=int, default=0, metavar="K",
+                    help="instead of the decode benchmark: prefill workload K (1: 4 x 4,100-token prompts, "
+                         "2: 16 x 100-token chunks over a shared 4,000-token prefix)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill summary in the decode line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="instead of the benchmark: run pa_block_copy over PAIRS distinct block pairs "
                          "(known bytes) 5 times, for scaling hardware byte counters")
@@ -122,6 +126,73 @@ def cpu_baseline(w, n_seqs: int):
             "seq_layers_per_s": len(sel) / dt}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, check: bool = True):
+    """Time pa_prefill on prefill workload k (chunk K/V written first by pa_cache_write).
+
+    Algorithmic work = the causal attention's multiply-adds: 4 * D * Hq flops
+    per (query row, visible key).  The bf16 high/low split of P is counted as
+    overhead, not as work."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    from workloads import PREFILL_NAMES, make_prefill
+    w = make_prefill(k)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    pool = pa.PagedKVPool(bf(w.pool))
+    tables = i32(w.block_tables)
+    slots = pa.pa_slot_mapping(pool, tables, i32(w.write_seq), i32(w.write_pos))
+    kn, vn = bf(w.k_new), bf(w.v_new)
+    pa.pa_cache_write(pool, kn, vn, slots)
+    q, qsl, lens = bf(w.q), i32(w.query_start_loc), i32(w.context_lens)
+    mq = int(np.diff(w.query_start_loc).max())
+    out = torch.empty((w.total_tokens, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+
+    def run():
+        pa.pa_prefill(pool, q, qsl, lens, tables, scale=float(w.scale), max_query_len=mq, out=out)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = w.attention_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    err = None
+    if check:  # one sampled row against the oracle (the first sequence's last row)
+        from oracle import paged
+        got = out.cpu().numpy()
+        n = int(w.query_start_loc[1])
+        ctx = int(w.context_lens[0])
+        nb = -(-ctx // w.block_size)
+        small = w.pool[w.block_tables[0, :nb]].copy()
+        tbl = np.arange(nb, dtype=np.int32)[None, :]
+        sl = paged.slot_mapping_ref(tbl, np.zeros(n, dtype=np.int32), w.write_pos[:n], w.block_size)
+        small = paged.cache_write_ref(small, w.k_new[:n], w.v_new[:n], sl)
+        want = paged.prefill_ref(small, w.q[n - 1:n], [0, 1], [ctx], tbl, float(w.scale))
+        err = float(np.abs(got[n - 1].astype(np.float64) - want[0]).max())
+    return {"workload": f"prefill workload {k}: {PREFILL_NAMES[k]}", "tokens": w.total_tokens,
+            "flops": flops, "us": round(ms * 1e3, 1), "tflops": round(tflops, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
+            "sampled_max_abs_err": err}
+
+
 def calibrate_copy(pairs: int, dev):
     """pa_block_copy of ``pairs`` distinct 64 KiB blocks (bf16, 8 KV heads, B16, D128):
     reads and writes exactly pairs * 65536 bytes per launch."""
@@ -157,6 +228,17 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, dev)
+        return
+    if args.prefill:
+        r = prefill_measurement(args.prefill, dev, reps=args.steps, warmup=args.warmup)
+        if r["sampled_max_abs_err"] is not None and not r["sampled_max_abs_err"] <= 2e-3:
+            print(f"[bench] PREFILL PARITY FAILURE: {r['sampled_max_abs_err']}", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"metric": "prefill attention TFLOP/s", "value": r["tflops"], "unit": "TFLOP/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                          "dtype": "bf16 Q/K/V, fp32 accumulate", "data": "synthetic",
+                          "config": {"workload": r["workload"], "tokens": r["tokens"]}, "us": r["us"],
+                          "roofline": r["roofline"], "sampled_max_abs_err": r["sampled_max_abs_err"]}), flush=True)
         return
     t_gen = time.perf_counter()
     w = make_config(args.workload)
@@ -251,6 +333,11 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seqs)
     host_bm = block_manager_timing(w)
+    prefill = None
+    if not args.no_prefill:
+        del pool, workspace, out, q
+        torch.cuda.empty_cache()
+        prefill = prefill_measurement(1, dev)
 
     line = {
         "metric": METRIC,
@@ -283,6 +370,7 @@ def main():
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
         "block_manager": host_bm,
+        "prefill": prefill,
         "sampled_max_abs_err": check,
     }
     print(json.dumps(line), flush=True)

@@ -8,12 +8,13 @@
 // over cached positions 0 .. p, found through the block table.
 //
 // Unlike decode this is a dense contraction, so it runs on the matrix cores
-// (v_mfma_f32_16x16x32_bf16).  One workgroup of 4 waves takes 64 query rows
-// of one KV head: rows are (head of the group, token) pairs, head-major, so
+// (v_mfma_f32_16x16x32_bf16).  One workgroup of 4 waves takes 128 query rows
+// of one KV head (32 per wave, two 16-row groups sharing every K and V
+// operand read): rows are (head of the group, token) pairs, head-major, so
 // every row of the workgroup reads the same K/V.  K/V tiles of 64 keys are
 // gathered through the block table into LDS (double-buffered, the next
 // tile's global loads in flight while the current one is used), and each
-// wave computes flash-attention style on its 16 rows:
+// wave computes flash-attention style on its rows:
 //   S^T = K Q^T   A = K rows from LDS (ds_read_b128, XOR-swizzled rows so 16
 //                 rows hit 16 different bank groups), B = Q^T held in
 //                 registers.  The C layout of S^T gives every lane one row
@@ -37,10 +38,17 @@
 namespace pa {
 namespace {
 
+#ifndef PA_PREFILL_ROW_GROUPS
+#define PA_PREFILL_ROW_GROUPS 1
+#endif
+
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kRows = 64;        // query rows per workgroup (16 per wave)
-constexpr int kKeys = 64;        // keys per LDS tile
+// 16-row groups per wave: every K or V operand read from LDS feeds RG
+// matrix-core instructions, so LDS traffic per flop falls as 1/RG.
+constexpr int kRG = PA_PREFILL_ROW_GROUPS;
+constexpr int kRows = 16 * kRG * kPfWaves;  // query rows per workgroup
+constexpr int kKeys = 64;                    // keys per LDS tile
 constexpr float kPfNegInf = -__builtin_inff();
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfRescaleThreshold = 8.0f;
@@ -54,6 +62,23 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Max / sum over the four 16-lane groups of the wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap permutes: with both operands the same value,
+// permlane16_swap yields the values of lanes (l & ~16, l | 16) and
+// permlane32_swap those of (l & ~32, l | 32) -- VALU only, no LDS round trip.
+__device__ __forceinline__ float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D>
 struct PfCfg {
@@ -81,8 +106,10 @@ __device__ __forceinline__ int v_lds8(int key, int c8) {
   return key * PfCfg<D>::ROWB + ((c8 ^ (4 * (key % (PfCfg<D>::NCH8 / 4)))) << 3);
 }
 
+// Two waves per SIMD: the register budget that lets two workgroups share a
+// compute unit (their LDS fits as well), so one's loads overlap the other's math.
 template <int D, int B, int G>
-__global__ void __launch_bounds__(kPfThreads)
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads, const char *__restrict__ q,
                float *__restrict__ out, const int32_t *__restrict__ query_start_loc,
                const int32_t *__restrict__ context_lens, const int32_t *__restrict__ tables,
@@ -121,29 +148,36 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     return;
   }
 
-  const int my_r = wave * 16 + r16;
-  const int my_t = row_token(my_r);
-  const bool my_active = my_t < n;
-  const int my_pos = my_active ? ctx - n + my_t : -1;
-
-  // Q^T operand: lane holds Q[row r16][kc*32 + 8*grp .. +8] for every kc
-  bf16x8_t qb[C::KC];
+  // rows of this wave: 16*kRG consecutive rows starting at wave*16*kRG;
+  // lane (r16, grp) owns row wave*16*kRG + 16*rg + r16 of group rg
+  int my_pos[kRG];
+  bool my_active[kRG];
+  bf16x8_t qb[kRG][C::KC];
 #pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (my_active) {
-      const char *p = q + ((((int64_t)q0 + my_t) * num_q_heads + hq0 + row_head(my_r)) * D + kc * 32 + 8 * grp) * 2;
-      v = *reinterpret_cast<const u32x4_t *>(p);
+  for (int rg = 0; rg < kRG; ++rg) {
+    const int r = wave * 16 * kRG + 16 * rg + r16;
+    const int t = row_token(r);
+    my_active[rg] = t < n;
+    my_pos[rg] = my_active[rg] ? ctx - n + t : -1;
+    // Q^T operand: lane holds Q[row][kc*32 + 8*grp .. +8] for every kc
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (my_active[rg]) {
+        const char *p = q + ((((int64_t)q0 + t) * num_q_heads + hq0 + row_head(r)) * D + kc * 32 + 8 * grp) * 2;
+        v = *reinterpret_cast<const u32x4_t *>(p);
+      }
+      qb[rg][kc] = as_bf16x8(v);
     }
-    qb[kc] = as_bf16x8(v);
   }
 
   // key range this workgroup needs, and per-wave bounds for skipping/masking
   const int last_t = min(qt * QT + QT, n) - 1;
   const int kv_end = ctx - n + last_t + 1;  // keys 0 .. kv_end-1
   const int ntiles = (kv_end + kKeys - 1) / kKeys;
-  int w_tmin = QT >= 16 ? (wave * 16) % QT : 0;
-  int w_tmax = QT >= 16 ? w_tmin + 15 : QT - 1;
+  constexpr int WR = 16 * kRG;  // rows per wave
+  int w_tmin = QT >= WR ? (wave * WR) % QT : 0;
+  int w_tmax = QT >= WR ? w_tmin + WR - 1 : QT - 1;
   w_tmin = qt * QT + w_tmin;
   w_tmax = min(qt * QT + w_tmax, n - 1);
   const bool wave_active = w_tmin <= w_tmax;
@@ -152,28 +186,46 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 
   if (tid == 0) s_poison = 0;
 
-  // ---- global -> registers -> LDS for one tile of kKeys keys
+  // ---- global -> registers -> LDS for one tile of kKeys keys.  The tile's
+  // block ids are uniform (scalar loads, validated once); every lane then
+  // issues its K/V loads unconditionally at in-bounds addresses (keys past
+  // the sequence read block 0 and are replaced by zeros), so no load waits
+  // on a per-lane table read and no branch splits the wave.
+  constexpr int NBT = kKeys / B;  // blocks per tile
   u32x4_t kr[C::LOADS], vr[C::LOADS];
   bool poisoned = false;
+  const int seq_blocks = (ctx + B - 1) / B;
   const char *head_base = pool + (int64_t)h * B * C::ROWB;
   const int64_t kv_half = (int64_t)num_kv_heads * B * C::ROWB;  // K tile to V tile of one block
+  const int32_t *table_row = tables + (int64_t)s * max_blocks_per_seq;
   auto load_tile = [&](int t) {
+    int blk[NBT];
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) {
+      const int jb = t * NBT + i;
+      int b = jb < seq_blocks ? table_row[jb] : 0;
+      b = __builtin_amdgcn_readfirstlane(b);
+      if (b < 0 || (int64_t)b >= num_blocks) {
+        poisoned = true;
+        b = 0;
+      }
+      blk[i] = b;
+    }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int c = tid + i * kPfThreads;
       const int key = c / C::NCH16, ch = c % C::NCH16;
-      const int j = t * kKeys + key;
-      kr[i] = vr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (j < ctx) {
-        int b = tables[(int64_t)s * max_blocks_per_seq + j / B];
-        if (b < 0 || (int64_t)b >= num_blocks) {
-          poisoned = true;
-          b = 0;
-        }
-        const char *p = head_base + (int64_t)b * 2 * kv_half + (j % B) * C::ROWB + ch * 16;
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p + kv_half));
-      }
+      const int slot = key / B;  // uniform per i for D = 128; two values for D = 64
+      int b = blk[0];
+#pragma unroll
+      for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
+      const char *p = head_base + (int64_t)b * 2 * kv_half + (key % B) * C::ROWB + ch * 16;
+      const bool valid = t * kKeys + key < ctx;
+      const u32x4_t kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+      const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p + kv_half));
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      kr[i] = valid ? kv : zero;
+      vr[i] = valid ? vv : zero;
     }
   };
   auto store_tile = [&](int buf) {
@@ -187,108 +239,132 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   };
 
   // ---- per-row state: running max (log2 units), partial sum of this lane's
-  // keys, and the output tile O[4*grp + jj][16*nt + r16]
-  float m = kPfNegInf, lpart = 0.0f;
-  f32x4_t o[C::NT];
+  // keys, and the output tiles O[4*grp + jj][16*nt + r16] of each row group
+  float m[kRG], lpart[kRG];
+  f32x4_t o[kRG][C::NT];
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rg = 0; rg < kRG; ++rg) {
+    m[rg] = kPfNegInf;
+    lpart[rg] = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) o[rg][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  auto compute_tile = [&](int t, int buf) {
+  // Per-lane LDS byte offsets of the operand reads for sub-tile 0; the
+  // sub-tile, key-step and buffer offsets are compile-time constants that
+  // fold into the instructions' immediate offsets (the swizzle term depends
+  // only on the lane because 16kt, 32ks and 16 are multiples of its period).
+  int k_base[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) k_base[kc] = k_lds<D>(r16, kc * 4 + grp);
+  int v_base[C::NT];
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) v_base[nt] = v_lds8<D>(4 * grp + r16 / 4, 4 * nt + (r16 & 3));
+
+  auto compute_tile = [&](int t, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     const int k0 = t * kKeys;
     if (!wave_active || k0 > w_pos_max) return;  // every key of the tile is after every row
     const char *kt_lds = s_k[buf];
-    // S^T sub-tiles: sacc[kt] = K[16kt .. +16] Q^T
-    f32x4_t sacc[4];
+    // S^T sub-tiles: sacc[rg][kt] = K[16kt .. +16] Q_rg^T; each K operand serves every row group
+    f32x4_t sacc[kRG][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const int key = 16 * kt + r16;
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) sacc[rg][kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_lds<D>(key, kc * 4 + grp)]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[kc], sacc[kt], 0, 0, 0);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          sacc[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
       }
     }
-    // scores of row r16, keys k0 + 16kt + 4grp + jj
     const bool full = k0 + kKeys - 1 <= w_pos_min;  // no key of the tile is masked for any row
-    float sc[4][4];
-    float mx = kPfNegInf;
+    bf16x8_t ph[kRG][2], pl[kRG][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int rg = 0; rg < kRG; ++rg) {
+      // scores of this lane's row, keys k0 + 16kt + 4grp + jj
+      float sc[4][4];
+      float mx = kPfNegInf;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = k0 + 16 * kt + 4 * grp + jj;
-        float v = sacc[kt][jj] * scale_log2;
-        if (!full && key > my_pos) v = kPfNegInf;
-        sc[kt][jj] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const bool upd = mn > m + kPfRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-      const float alpha = upd ? pf_exp2(m - mn) : 1.0f;
-      if (upd) m = mn;
-      lpart *= alpha;
-      // O rows are 4*grp + jj: fetch those rows' factors
-      float ar[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) o[nt][jj] *= ar[jj];
-    }
-    const float ms = m == kPfNegInf ? 0.0f : m;
-    // P = exp2(s - m), split into bf16 high and low parts, in the permuted key order
-    bf16x8_t ph[2], pl[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float pv = pf_exp2(sc[2 * ks + half][jj] - ms);
-          lpart += pv;
-          const __bf16 hi = (__bf16)pv;
-          ph[ks][4 * half + jj] = hi;
-          pl[ks][4 * half + jj] = (__bf16)(pv - (float)hi);
+          const int key = k0 + 16 * kt + 4 * grp + jj;
+          float v = sacc[rg][kt][jj] * scale_log2;
+          if (!full && key > my_pos[rg]) v = kPfNegInf;
+          sc[kt][jj] = v;
+          mx = fmaxf(mx, v);
         }
-    // O += P V: V operand by transpose reads, keys in the same permuted order
+      mx = group_max(mx);
+      const float mn = fmaxf(m[rg], mx);
+      const bool upd = mn > m[rg] + kPfRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        const float alpha = upd ? pf_exp2(m[rg] - mn) : 1.0f;
+        if (upd) m[rg] = mn;
+        lpart[rg] *= alpha;
+        // O rows are 4*grp + jj: fetch those rows' factors
+        float ar[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) o[rg][nt][jj] *= ar[jj];
+      }
+      const float ms = m[rg] == kPfNegInf ? 0.0f : m[rg];
+      // P = exp2(s - m), split into bf16 high and low parts, in the permuted key order
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float pv = pf_exp2(sc[2 * ks + half][jj] - ms);
+            lpart[rg] += pv;
+            const __bf16 hi = (__bf16)pv;
+            ph[rg][ks][4 * half + jj] = hi;
+            pl[rg][ks][4 * half + jj] = (__bf16)(pv - (float)hi);
+          }
+    }
+    // O += P V: V operand by transpose reads, keys in the same permuted order; each serves every row group
     const char *vt_lds = s_v[buf];
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        i16x4_t lo4, hi4;
-        {
-          const int key = 32 * ks + 4 * grp + r16 / 4;
-          lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + v_lds8<D>(key, 4 * nt + (r16 & 3))));
-        }
-        {
-          const int key = 32 * ks + 16 + 4 * grp + r16 / 4;
-          hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + v_lds8<D>(key, 4 * nt + (r16 & 3))));
-        }
+        const i16x4_t lo4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
+        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
         const bf16x8_t vb = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[ks], vb, o[nt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg) {
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb, o[rg][nt], 0, 0, 0);
+        }
       }
     }
   };
 
-  // ---- main loop over key tiles
+  // ---- main loop over key tiles, unrolled by two so each half uses a fixed
+  // LDS buffer (its offsets are immediates)
+  using buf0 = std::integral_constant<int, 0>;
+  using buf1 = std::integral_constant<int, 1>;
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-    compute_tile(t, t & 1);
-    if (more) store_tile((t + 1) & 1);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+    compute_tile(t, buf0{});
+    if (t + 1 < ntiles) store_tile(1);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) load_tile(t + 2);
+    compute_tile(t + 1, buf1{});
+    if (t + 2 < ntiles) store_tile(0);
     __syncthreads();
   }
   if (poisoned) s_poison = 1;
@@ -296,21 +372,23 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   const bool seq_poisoned = s_poison != 0;
 
   // ---- normalise and store: row totals, then each O row divided by its total
-  float lrow = lpart + __shfl_xor(lpart, 16);
-  lrow += __shfl_xor(lrow, 32);
-  const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
-  float inv_r[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) inv_r[jj] = __shfl(inv, 4 * grp + jj);
+  for (int rg = 0; rg < kRG; ++rg) {
+    const float lrow = group_sum(lpart[rg]);
+    const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
+    float inv_r[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int r = wave * 16 + 4 * grp + jj;
-    const int tok = row_token(r);
-    if (tok >= n) continue;
-    float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
+    for (int jj = 0; jj < 4; ++jj) inv_r[jj] = __shfl(inv, 4 * grp + jj);
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt)
-      dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[nt][jj] * inv_r[jj];
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = wave * 16 * kRG + 16 * rg + 4 * grp + jj;
+      const int tok = row_token(r);
+      if (tok >= n) continue;
+      float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[rg][nt][jj] * inv_r[jj];
+    }
   }
 }
 
