@@ -14,6 +14,8 @@ cites step by step with no blocking, fusion or reordering:
                     null block, reference counts, on-demand growth,
                     copy-on-write decision).
 * ``accounting`` -- block counts, slot usage and waste, KV byte sizes.
+* ``prefix``     -- prefix caching: chained block hashes, the table of
+                    cached blocks, hits capped at the prompt minus one.
 
 Citation keys used in docstrings (page title, then section):
 
@@ -31,4 +33,4 @@ against values the pages print, brute force, closed forms or invariants,
 except where a docstring says "parity unpinned".
 """
 
-from . import accounting, alloc, paged  # noqa: F401
+from . import accounting, alloc, paged, prefix  # noqa: F401

@@ -162,8 +162,13 @@ def prepare_write(pool: BlockPool, seq: Sequence, token_index: int):
 
 
 def release_sequence(pool: BlockPool, seq: Sequence, reusable: bool = False) -> None:
-    """Return every block of a finished request ([HRL] §18 step 8; [TSS] "Paging")."""
-    for block in seq.block_table:
+    """Return every block of a finished request ([HRL] §18 step 8; [TSS] "Paging").
+
+    The pages leave the order open; the blocks are released last to first,
+    so that of a request's reusable blocks (back of the queue) the tail is
+    taken first and a cached chain of blocks is lost from its end.
+    """
+    for block in reversed(seq.block_table):
         pool.release(block, reusable=reusable)
     seq.block_table = []
     seq.num_tokens = 0
