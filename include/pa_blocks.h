@@ -16,7 +16,9 @@
  *           block with more than one reference first clones it to a fresh
  *           block, drops one reference of the original and repoints only
  *           the writer's table;
- *   [TSS]   "Finding a token": slot = block * block_size + offset.
+ *   [TSS]   "Finding a token": slot = block * block_size + offset;
+ *   [TSS]   "Sharing a prefix: one copy for many requests": prefix caching
+ *           (see the prefix caching section below).
  *
  * Everything here runs on the host and touches no device memory: it emits
  * the slots, copy-on-write pairs and block tables that pa.h's kernels take.
@@ -74,7 +76,9 @@ int pa_bm_allocate_prompt(pa_block_manager *bm, int64_t seq, int32_t num_tokens)
  * then copy-on-write if the block holding it has more than one reference.
  * *slot receives the token's slot; *cow_src / *cow_dst receive the block
  * pair to copy before the write, or -1 when none is needed.  The sequence's
- * token count becomes max(count, position + 1).
+ * token count becomes max(count, position + 1).  The block written leaves
+ * the prefix cache if it was in it (its contents change); a position whose
+ * token id was committed (pa_bm_commit_tokens) is PA_ERR_INVALID_ARG.
  */
 int pa_bm_prepare_write(pa_block_manager *bm, int64_t seq, int32_t position, int64_t *slot, int32_t *cow_src,
                         int32_t *cow_dst);
@@ -91,9 +95,10 @@ int pa_bm_append_tokens(pa_block_manager *bm, const int64_t *seqs, int32_t n, in
                         int32_t *cow_src_out, int32_t *cow_dst_out, int32_t *num_cow_out);
 
 /*
- * Release every block of `seq` and forget it ([HRL] section 18 step 8).
- * Blocks reaching zero references go to the back of the free queue when
- * reusable != 0, else to the front.
+ * Release every block of `seq`, last block first, and forget it ([HRL]
+ * section 18 step 8).  Blocks reaching zero references go to the back of the
+ * free queue when reusable != 0 or when they are in the prefix cache (they
+ * keep their digest until an allocation takes them), else to the front.
  */
 int pa_bm_free_sequence(pa_block_manager *bm, int64_t seq, int32_t reusable);
 
@@ -104,6 +109,65 @@ int pa_bm_free_sequence(pa_block_manager *bm, int64_t seq, int32_t reusable);
  */
 int pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t max_blocks_per_seq,
                        int32_t pad_value, int32_t *tables_out, int32_t *lens_out);
+
+/*
+ * ---- Prefix caching ([TSS] "Sharing a prefix: one copy for many requests").
+ *
+ * Each full block of a sequence whose token ids are known has a 32-byte
+ * digest chained over everything before it: d_j = SHA-256(d_{j-1} || ids of
+ * block j as little-endian int32), d_{-1} = 32 zero bytes (the page fixes
+ * the inputs of the hash, not the function; SHA-256 is FIPS 180-4).  The
+ * manager keeps a table digest -> block.  A block enters the table when its
+ * last id is known (pa_bm_allocate_prompt_cached, pa_bm_commit_tokens)
+ * unless the block already has a digest or the digest already has a block;
+ * it leaves when an allocation takes it from the free queue (eviction) or a
+ * write changes it.  Partial blocks are never in the table.
+ */
+
+/*
+ * Chained digests of the full blocks of tokens[num_tokens] (ids as given),
+ * starting from `parent` (32 bytes; NULL: zeros), into digests_out
+ * [num_tokens / block_size][32].  Returns the number of full blocks.
+ * Stateless; needs no manager.
+ */
+int pa_bm_hash_blocks(const int32_t *tokens, int64_t num_tokens, int32_t block_size, const uint8_t *parent,
+                      uint8_t *digests_out);
+
+/*
+ * How many tokens of a prompt tokens[num_tokens] are found in the cache: the
+ * longest run of leading blocks whose digests are in the table, at most
+ * floor((num_tokens - 1) / block_size) blocks (a prompt always computes at
+ * least its last token), times block_size.  Changes nothing.
+ */
+int pa_bm_lookup_prefix(pa_block_manager *bm, const int32_t *tokens, int32_t num_tokens,
+                        int32_t *num_cached_tokens);
+
+/*
+ * Prefill allocation with prefix caching for an empty sequence: the cached
+ * leading blocks (as pa_bm_lookup_prefix finds them) are touched -- one more
+ * reference, off the free queue if idle -- and head the table; the rest of
+ * ceil(num_tokens / block_size) blocks come from the free queue.  The ids
+ * are committed and every full block of the prompt enters the table.
+ * *num_cached_tokens receives the tokens whose K/V need not be computed.
+ * All or nothing (PA_ERR_OUT_OF_BLOCKS); a sequence with blocks or tokens
+ * already is PA_ERR_INVALID_ARG.
+ */
+int pa_bm_allocate_prompt_cached(pa_block_manager *bm, int64_t seq, const int32_t *tokens, int32_t num_tokens,
+                                 int32_t *num_cached_tokens);
+
+/*
+ * Commit the ids of the next n tokens of `seq` (after those already
+ * committed; they must lie within its token count, i.e. their slots were
+ * prepared) and enter every block they complete.  A forked sequence starts
+ * with its parent's ids over the shared span.
+ */
+int pa_bm_commit_tokens(pa_block_manager *bm, int64_t seq, const int32_t *ids, int32_t n);
+
+/* Blocks in the prefix cache table. */
+int64_t pa_bm_num_cached(const pa_block_manager *bm);
+
+/* 1 and the block's digest into digest_out[32] if it is in the table, else 0. */
+int pa_bm_block_digest(const pa_block_manager *bm, int32_t block, uint8_t *digest_out);
 
 /* Queries: counts, one block's references, one sequence's shape, the queue. */
 int64_t pa_bm_num_free(const pa_block_manager *bm);

@@ -12,7 +12,10 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 * the host block manager of ``include/pa_blocks.h``: ``pa_bm_create``,
   ``pa_bm_add_sequence``, ``pa_bm_fork``, ``pa_bm_allocate_prompt``,
   ``pa_bm_prepare_write``, ``pa_bm_append_tokens``, ``pa_bm_free_sequence``,
-  ``pa_bm_block_tables`` and the queries (host numpy arrays in and out)
+  ``pa_bm_block_tables`` and the queries (host numpy arrays in and out);
+  prefix caching: ``pa_bm_hash_blocks``, ``pa_bm_lookup_prefix``,
+  ``pa_bm_allocate_prompt_cached``, ``pa_bm_commit_tokens``,
+  ``pa_bm_num_cached``, ``pa_bm_block_digest``
 
 Tensors live on a ROCm device (torch provides memory and the current
 stream).  There is no fallback: if libpa.so is missing or the device is not
@@ -35,13 +38,19 @@ __all__ = [
     "pa_block_copy",
     "pa_bm_add_sequence",
     "pa_bm_allocate_prompt",
+    "pa_bm_allocate_prompt_cached",
     "pa_bm_append_tokens",
+    "pa_bm_block_digest",
     "pa_bm_block_tables",
+    "pa_bm_commit_tokens",
     "pa_bm_create",
     "pa_bm_destroy",
     "pa_bm_fork",
     "pa_bm_free_queue",
     "pa_bm_free_sequence",
+    "pa_bm_hash_blocks",
+    "pa_bm_lookup_prefix",
+    "pa_bm_num_cached",
     "pa_bm_num_free",
     "pa_bm_num_sequences",
     "pa_bm_prepare_write",
@@ -116,6 +125,12 @@ _SIGNATURES = {
     "pa_bm_refcount": (_I32, [_VP, _I32]),
     "pa_bm_sequence_info": (_I32, [_VP, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "pa_bm_free_queue": (_I64, [_VP, _VP, _I64]),
+    "pa_bm_hash_blocks": (_I32, [_VP, _I64, _I32, _VP, _VP]),
+    "pa_bm_lookup_prefix": (_I32, [_VP, _VP, _I32, ctypes.POINTER(_I32)]),
+    "pa_bm_allocate_prompt_cached": (_I32, [_VP, _I64, _VP, _I32, ctypes.POINTER(_I32)]),
+    "pa_bm_commit_tokens": (_I32, [_VP, _I64, _VP, _I32]),
+    "pa_bm_num_cached": (_I64, [_VP]),
+    "pa_bm_block_digest": (_I32, [_VP, _I32, _VP]),
 }
 PA_ERR_OUT_OF_BLOCKS = -5
 
@@ -478,3 +493,57 @@ def pa_bm_free_queue(bm):
     out = np.empty(max(n, 1), dtype=np.int32)
     lib.pa_bm_free_queue(bm, out.ctypes.data, n)
     return out[:n].copy()
+
+
+# ------------------------------------------------------------------ prefix caching
+
+
+def pa_bm_hash_blocks(tokens, block_size: int, parent: bytes | None = None):
+    """Chained digests of the full blocks of ``tokens``: uint8 [n // block_size][32]."""
+    np = _np()
+    tokens = _host(tokens, "int32")
+    full = len(tokens) // block_size if block_size > 0 else 0
+    out = np.empty((max(full, 1), 32), dtype=np.uint8)
+    par = None
+    if parent is not None:
+        if len(parent) != 32:
+            raise ValueError("parent digest must be 32 bytes")
+        par = ctypes.create_string_buffer(bytes(parent), 32)
+    r = load_library().pa_bm_hash_blocks(tokens.ctypes.data, len(tokens), block_size, par, out.ctypes.data)
+    _check(min(r, 0), "pa_bm_hash_blocks")
+    return out[:r].copy()
+
+
+def pa_bm_lookup_prefix(bm, tokens) -> int:
+    """Tokens of ``tokens`` a prompt would find cached (nothing changes)."""
+    tokens = _host(tokens, "int32")
+    n = ctypes.c_int32()
+    _check(load_library().pa_bm_lookup_prefix(bm, tokens.ctypes.data, len(tokens), ctypes.byref(n)),
+           "pa_bm_lookup_prefix")
+    return n.value
+
+
+def pa_bm_allocate_prompt_cached(bm, seq: int, tokens) -> int:
+    """Prefill allocation with prefix caching; returns the number of cached tokens."""
+    tokens = _host(tokens, "int32")
+    n = ctypes.c_int32()
+    _check(load_library().pa_bm_allocate_prompt_cached(bm, seq, tokens.ctypes.data, len(tokens), ctypes.byref(n)),
+           "pa_bm_allocate_prompt_cached")
+    return n.value
+
+
+def pa_bm_commit_tokens(bm, seq: int, ids) -> None:
+    ids = _host(ids, "int32")
+    _check(load_library().pa_bm_commit_tokens(bm, seq, ids.ctypes.data, len(ids)), "pa_bm_commit_tokens")
+
+
+def pa_bm_num_cached(bm) -> int:
+    return int(load_library().pa_bm_num_cached(bm))
+
+
+def pa_bm_block_digest(bm, block: int):
+    """The block's digest (32 bytes) while it is in the prefix cache, else None."""
+    buf = ctypes.create_string_buffer(32)
+    r = load_library().pa_bm_block_digest(bm, block, buf)
+    _check(min(r, 0), "pa_bm_block_digest")
+    return buf.raw if r == 1 else None

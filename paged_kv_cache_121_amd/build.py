@@ -50,7 +50,7 @@ def _compile(src: str, hipcc: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     if src.endswith(".cpp"):
         cxx = shutil.which("g++") or "g++"
-        cmd = [cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", f"-I{CSRC}",
+        cmd = [cxx, "-O3", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", f"-I{CSRC}",
                f"-I{ROCM_INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
     else:
         cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]

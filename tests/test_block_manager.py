@@ -195,7 +195,7 @@ def test_null_block_and_free_ordering():
     p.allocate_prompt(t, 4)    # none left
     p.free(s, reusable=True)
     p.check()
-    assert pa.pa_bm_free_queue(p.bm).tolist() == [1, 2, 3, 4, 5]
+    assert pa.pa_bm_free_queue(p.bm).tolist() == [5, 4, 3, 2, 1]  # released last to first
     p.close()
 
 

@@ -12,8 +12,10 @@ from .configs import (  # noqa: F401
     CONFIG_NAMES,
     PREFILL_NAMES,
     PrefillWorkload,
+    TokenModel,
     make_prefill,
     make_prefill_custom,
+    make_token_model,
     Step,
     Workload,
     make_config,

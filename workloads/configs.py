@@ -413,3 +413,44 @@ def make_prefill(k: int, small: bool = False) -> PrefillWorkload:
                                    block_size=16, context_lens=[prefix + chunk] * S, chunk_lens=[chunk] * S,
                                    shared_prefix_tokens=prefix)
     raise ValueError(f"no prefill workload {k}")
+
+
+# ---------------------------------------------------------------- token-determined K/V for prefix caching
+
+
+@dataclass
+class TokenModel:
+    """Stand-in for a model layer whose K, V and Q depend only on (token id, position).
+
+    Two prompts with the same leading tokens then hold bit-identical K/V over
+    that prefix, which is what lets a cached block stand in for recomputing
+    it.  Values are embedding-plus-position sums rounded to bf16; nothing of
+    the attention method is computed here.
+    """
+
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    embed: np.ndarray  # float32 [vocab][Hq + 2 Hkv][D]
+    pos: np.ndarray    # float32 [max_pos][Hq + 2 Hkv][D]
+
+    def _rows(self, ids, positions):
+        ids = np.asarray(ids, dtype=np.int64)
+        positions = np.asarray(positions, dtype=np.int64)
+        return self.embed[ids] + self.pos[positions]
+
+    def qkv(self, ids, positions):
+        """(q [T][Hq][D], k [T][Hkv][D], v [T][Hkv][D]) as bf16 bit patterns."""
+        x = to_bf16_bits(self._rows(ids, positions))
+        hq, hkv = self.num_q_heads, self.num_kv_heads
+        return (np.ascontiguousarray(x[:, :hq]), np.ascontiguousarray(x[:, hq:hq + hkv]),
+                np.ascontiguousarray(x[:, hq + hkv:]))
+
+
+def make_token_model(seed: int, vocab: int, max_pos: int, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int) -> TokenModel:
+    rng = np.random.default_rng(seed)
+    rows = num_q_heads + 2 * num_kv_heads
+    embed = rng.standard_normal((vocab, rows, head_dim), dtype=np.float32)
+    pos = 0.5 * rng.standard_normal((max_pos, rows, head_dim), dtype=np.float32)
+    return TokenModel(num_q_heads, num_kv_heads, head_dim, embed, pos)
