@@ -70,8 +70,11 @@ typedef enum { PA_DECODE_STREAM = 0, PA_DECODE_KEEP_CACHED = 1 } pa_decode_flags
  * elements laid out as [num_blocks][2][num_kv_heads][block_size][head_dim]:
  * index 0 of the second axis holds K and index 1 holds V, so one physical
  * block is one contiguous chunk and each (block, head) K or V tile is
- * contiguous.  Supported: block_size 16 or 32, head_dim 64 or 128, dtype
- * PA_F32 or PA_BF16 (bf16 = upper half of an IEEE binary32).
+ * contiguous.  Supported: block_size a power of two up to 256 (slot
+ * mapping, cache write, block copy, swap), of which pa_decode and
+ * pa_prefill take 4, 8, 16, 32, 64 and 128 ([AINEW] block-size figure, 4 /
+ * 16 / 64; [VIBE] evaluation, 16 to 128); head_dim 64 or 128; dtype PA_F32
+ * or PA_BF16 (bf16 = upper half of an IEEE binary32).
  */
 typedef struct {
   void *base;
@@ -154,8 +157,8 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
  *   scale        : multiplier of q.k (usually 1/sqrt(head_dim)).
  *   max_context_len : host-known upper bound of context_lens.
  *   partition_size  : tokens per split-context partition; 0 = automatic;
- *                  else a positive multiple of block_size, at most 512
- *                  blocks.
+ *                  else a positive multiple of max(block_size, 16), at
+ *                  most 512 blocks.
  *   flags        : PA_DECODE_STREAM or PA_DECODE_KEEP_CACHED (see above).
  *   workspace    : scratch for split-context partial results, at least
  *                  pa_decode_workspace_size() bytes, 256-byte aligned (may

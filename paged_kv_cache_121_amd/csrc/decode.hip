@@ -224,7 +224,12 @@ struct Cfg {
   static constexpr int NW = VEC / 4;             // 32-bit words per lane per token
   static constexpr int QS = G < 4 ? G : 4;       // quad lanes that own distinct heads
   static constexpr int HPL = G / QS;             // heads owned per lane
-  static constexpr int CPB = B / kChunk;         // pipeline stages per block
+  // A pipeline stage is kChunk consecutive tokens.  Large blocks hold CPB
+  // stages; small blocks (B = 4, 8) are grouped R to a stage.  A "unit" is
+  // the span a wave takes at a time: one block, or R consecutive blocks.
+  static constexpr int R = B < kChunk ? kChunk / B : 1;    // blocks per unit
+  static constexpr int CPB = B < kChunk ? 1 : B / kChunk;  // pipeline stages per unit
+  static constexpr int UNIT = R * B;                       // tokens per unit
   static constexpr int64_t ROW = (int64_t)D * kElem;
   static constexpr int64_t TILE = (int64_t)B * ROW;
   static constexpr int64_t CHUNK = (int64_t)kChunk * ROW;
@@ -244,7 +249,8 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
               float scale_log2, int max_context_len, int part_blocks, int max_parts,
               float *__restrict__ ws_o, float *__restrict__ ws_ml) {
   using C = Cfg<T, D, B, G>;
-  constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB;
+  constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB, R = C::R;
+  static_assert(B % 4 == 0 && (B < kChunk ? kChunk % B == 0 : B % kChunk == 0), "block size");
 
   __shared__ int s_tbl[kMaxPartitionBlocks];
   __shared__ float s_o[kWaves][G][D];
@@ -275,8 +281,12 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   const int nblk = min(part_blocks, seq_blocks - blk_begin);
   if (tid == 0) s_poison = 0;
   __syncthreads();
-  for (int i = tid; i < nblk; i += kThreads) {
-    int b = tables[(int64_t)s * max_blocks_per_seq + blk_begin + i];
+  // The last unit of a sequence of small blocks may reach past its blocks:
+  // those entries read block 0 (in bounds) and all their tokens are masked.
+  // Partitions hold whole units, so nunits * R <= part_blocks.
+  const int nunits = (nblk + R - 1) / R;
+  for (int i = tid; i < nunits * R; i += kThreads) {
+    int b = i < nblk ? tables[(int64_t)s * max_blocks_per_seq + blk_begin + i] : 0;
     if (b < 0 || (int64_t)b >= num_blocks) {
       s_poison = 1;
       b = 0;
@@ -303,24 +313,38 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.0f;
 
-  const int nb_w = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int nb_w = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
   const int nch = nb_w * CPB;
   const char *kv_head_base = pool + (int64_t)h * C::TILE;
   const int64_t v_off = (int64_t)num_kv_heads * C::TILE;
   const int lane_off = lane * C::VEC;
 
   auto issue = [&](int ci, Frag<NW> (&kf)[4], Frag<NW> (&vf)[4]) {
-    const int lb = wave + (ci / CPB) * kWaves;
-    const int sub = ci % CPB;
-    const int phys = __builtin_amdgcn_readfirstlane(s_tbl[lb]);
-    const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
+    const int unit = wave + (ci / CPB) * kWaves;
+    if constexpr (R == 1) {
+      const int sub = ci % CPB;
+      const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
+      const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp + j * C::STEP);
+      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp + j * C::STEP);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp + v_off + j * C::STEP);
+      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp + v_off + j * C::STEP);
+    } else {
+      // load step j (4 tokens) lies in block 4j / B of the unit, at row 4j % B
+      const char *kp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit * R + (4 * j) / B]);
+        kp[j] = kv_head_base + (int64_t)phys * (2 * v_off) + ((4 * j) % B) * C::ROW + lane_off;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp[j] + v_off);
+    }
   };
   auto process = [&](int ci, const Frag<NW> (&kf)[4], const Frag<NW> (&vf)[4]) {
-    const int tok0 = (blk_begin + wave + (ci / CPB) * kWaves) * B + (ci % CPB) * kChunk;
+    const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * kChunk;
     const bool partial = tok0 + kChunk > L;
     // QK for the 4 tokens this row sees in the chunk
     float sc[4][HPL];
@@ -554,8 +578,12 @@ hipError_t dispatch_group(const DecodeArgs &a, int group, hipStream_t stream) {
 template <typename T, int D>
 hipError_t dispatch_block(const DecodeArgs &a, int group, hipStream_t stream) {
   switch (a.pool.block_size) {
+    case 4: return dispatch_group<T, D, 4>(a, group, stream);
+    case 8: return dispatch_group<T, D, 8>(a, group, stream);
     case 16: return dispatch_group<T, D, 16>(a, group, stream);
     case 32: return dispatch_group<T, D, 32>(a, group, stream);
+    case 64: return dispatch_group<T, D, 64>(a, group, stream);
+    case 128: return dispatch_group<T, D, 128>(a, group, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -573,7 +601,8 @@ hipError_t dispatch_dim(const DecodeArgs &a, int group, hipStream_t stream) {
 
 bool decode_supported(int dtype, int head_dim, int block_size, int group) {
   return (dtype == PA_F32 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
-         (block_size == 16 || block_size == 32) && (group == 1 || group == 2 || group == 4 || group == 8);
+         (block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 ||
+          block_size == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {

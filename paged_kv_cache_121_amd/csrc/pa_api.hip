@@ -26,7 +26,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int check_pool(const pa_pool *p, PoolDesc *d) {
   if (p == nullptr || p->base == nullptr) return PA_ERR_INVALID_ARG;
   if (p->num_blocks <= 0 || p->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
-  if (p->block_size != 16 && p->block_size != 32) return PA_ERR_UNSUPPORTED;
+  // any power of two up to 256 for the data-movement kernels; attention
+  // kernels check their own block sizes
+  if (p->block_size <= 0 || p->block_size > 256 || (p->block_size & (p->block_size - 1)) != 0)
+    return PA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (p->dtype != PA_F32 && p->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
@@ -47,14 +50,18 @@ int check_pool(const pa_pool *p, PoolDesc *d) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+int partition_unit(int block_size) { return block_size < 16 ? 16 : block_size; }
+
 int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   const int64_t want_parts = pairs >= kMinWorkgroups ? 1 : (kMinWorkgroups + pairs - 1) / pairs;
   int64_t part = (max_context_len + want_parts - 1) / want_parts;
   if (pairs >= kManyPairs && part > kSkewedPartitionTokens) part = kSkewedPartitionTokens;
   if (part < kMinAutoPartitionTokens) part = kMinAutoPartitionTokens;
-  part = (part + block_size - 1) / block_size * block_size;
-  const int64_t cap = (int64_t)kMaxPartitionBlocks * block_size;
+  // partitions hold whole decode units (one block, or 16 tokens of small blocks)
+  const int unit = partition_unit(block_size);
+  part = (part + unit - 1) / unit * unit;
+  const int64_t cap = (int64_t)kMaxPartitionBlocks * block_size / unit * unit;
   if (part > cap) part = cap;
   return (int)part;
 }
@@ -63,7 +70,7 @@ int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int ma
 int resolve_partition(const PoolDesc &pool, int num_seqs, int max_context_len, int partition_size) {
   if (partition_size == 0)
     return auto_partition_tokens(pool.block_size, num_seqs, pool.num_kv_heads, max_context_len);
-  if (partition_size < 0 || partition_size % pool.block_size != 0) return PA_ERR_INVALID_ARG;
+  if (partition_size < 0 || partition_size % partition_unit(pool.block_size) != 0) return PA_ERR_INVALID_ARG;
   if (partition_size / pool.block_size > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
   return partition_size;
 }

@@ -191,7 +191,10 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // issues its K/V loads unconditionally at in-bounds addresses (keys past
   // the sequence read block 0 and are replaced by zeros), so no load waits
   // on a per-lane table read and no branch splits the wave.
-  constexpr int NBT = kKeys / B;  // blocks per tile
+  // A tile spans NBT whole blocks (B <= kKeys) or a kKeys-key slice of one
+  // block (B > kKeys).
+  constexpr int NBT = B <= kKeys ? kKeys / B : 1;
+  static_assert(B % 4 == 0 && (B <= kKeys ? kKeys % B == 0 : B % kKeys == 0), "block size");
   u32x4_t kr[C::LOADS], vr[C::LOADS];
   bool poisoned = false;
   const int seq_blocks = (ctx + B - 1) / B;
@@ -202,7 +205,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     int blk[NBT];
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
-      const int jb = t * NBT + i;
+      const int jb = B <= kKeys ? t * NBT + i : t / (B / kKeys);
       int b = jb < seq_blocks ? table_row[jb] : 0;
       b = __builtin_amdgcn_readfirstlane(b);
       if (b < 0 || (int64_t)b >= num_blocks) {
@@ -215,11 +218,17 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     for (int i = 0; i < C::LOADS; ++i) {
       const int c = tid + i * kPfThreads;
       const int key = c / C::NCH16, ch = c % C::NCH16;
-      const int slot = key / B;  // uniform per i for D = 128; two values for D = 64
       int b = blk[0];
+      int row_in_block;
+      if constexpr (B <= kKeys) {
+        const int slot = key / B;  // uniform per i for D = 128 and B >= 16
 #pragma unroll
-      for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
-      const char *p = head_base + (int64_t)b * 2 * kv_half + (key % B) * C::ROWB + ch * 16;
+        for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
+        row_in_block = key % B;
+      } else {
+        row_in_block = (t % (B / kKeys)) * kKeys + key;
+      }
+      const char *p = head_base + (int64_t)b * 2 * kv_half + row_in_block * C::ROWB + ch * 16;
       const bool valid = t * kKeys + key < ctx;
       const u32x4_t kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
       const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p + kv_half));
@@ -417,8 +426,12 @@ hipError_t prefill_group(const PrefillArgs &a, int group, hipStream_t stream) {
 template <int D>
 hipError_t prefill_block(const PrefillArgs &a, int group, hipStream_t stream) {
   switch (a.pool.block_size) {
+    case 4: return prefill_group<D, 4>(a, group, stream);
+    case 8: return prefill_group<D, 8>(a, group, stream);
     case 16: return prefill_group<D, 16>(a, group, stream);
     case 32: return prefill_group<D, 32>(a, group, stream);
+    case 64: return prefill_group<D, 64>(a, group, stream);
+    case 128: return prefill_group<D, 128>(a, group, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -426,7 +439,9 @@ hipError_t prefill_block(const PrefillArgs &a, int group, hipStream_t stream) {
 }  // namespace
 
 bool prefill_supported(int dtype, int head_dim, int block_size, int group) {
-  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32) &&
+  const bool b_ok = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 ||
+                    block_size == 64 || block_size == 128;
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && b_ok &&
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 

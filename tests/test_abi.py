@@ -51,9 +51,19 @@ def test_host_side_argument_checks_without_a_gpu():
     ref = ctypes.byref
     assert lib.pa_decode_partition_size(ref(good), 3, 4, 47) == 256
     # block size, head dim, dtype outside the built kernels
-    for bad in (pa.pa_pool(0x1000, 16, 4, 8, 64, 0), pa.pa_pool(0x1000, 16, 4, 16, 96, 0),
+    for bad in (pa.pa_pool(0x1000, 16, 4, 12, 64, 0), pa.pa_pool(0x1000, 16, 4, 512, 64, 0),
+                pa.pa_pool(0x1000, 16, 4, 0, 64, 0), pa.pa_pool(0x1000, 16, 4, 16, 96, 0),
                 pa.pa_pool(0x1000, 16, 4, 16, 64, 7)):
         assert lib.pa_cache_write(ref(bad), 1, 1, 1, 1, None) == -2
+    # block sizes: the attention kernels take 4..128; smaller blocks need partitions of whole
+    # 16-token units
+    b2 = pa.pa_pool(0x1000, 64, 4, 2, 64, pa.PA_F32)
+    assert lib.pa_decode(ref(b2), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 0, 0, None, 0, None) == -2
+    assert lib.pa_prefill(ref(pa.pa_pool(0x1000, 64, 4, 2, 64, pa.PA_BF16)), 1, 1, 1, 1, 1, 4, 3, 4, 10, 10, 0.1,
+                          None) == -2
+    b4 = pa.pa_pool(0x1000, 64, 4, 4, 64, pa.PA_F32)
+    assert lib.pa_decode(ref(b4), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 8, 0, None, 0, None) == -1
+    assert lib.pa_decode_partition_size(ref(b4), 3, 4, 47) % 16 == 0
     # null pool base, negative sizes
     assert lib.pa_block_copy(ref(pa.pa_pool(None, 16, 4, 16, 64, 0)), 1, 1, 1, None) == -1
     assert lib.pa_block_copy(ref(good), 1, 1, -1, None) == -1

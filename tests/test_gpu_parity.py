@@ -255,6 +255,28 @@ def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows():
     assert np.abs(out[good] - want).max() <= ATOL
 
 
+@pytest.mark.parametrize("block_size", [4, 8, 64, 128])
+@pytest.mark.parametrize("group,head_dim,dtype", [(4, 128, "bf16"), (8, 64, "f32"), (1, 128, "bf16")])
+def test_decode_block_size_sweep(block_size, group, head_dim, dtype):
+    # small blocks are taken 16 / B to a pipeline stage, large ones in 16-token stages;
+    # lengths land inside a stage, on its edge and one past it
+    hkv = 2
+    lens = [1, 5, 9, 16, 17, 63, 129, 300]
+    nb = sum(-(-L // block_size) for L in lens) + 8
+    w = make_custom(name="block-size-sweep", seed=43 + block_size, dtype=dtype, num_blocks=nb,
+                    num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=head_dim, block_size=block_size,
+                    lengths=lens)
+    say(f"[block sizes] B={block_size} G={group} D={head_dim} {dtype}")
+    for part in (0, 2 * max(block_size, 16)):
+        pool = device_pool(w)
+        _, out = run_step(w, pool, i32(w.block_tables), 0, partition_size=part)
+        _, pool_np = oracle_step(w, w.pool, 0)
+        want = decode_oracle(w, pool_np, 0)
+        err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+        say(f"    partition {part}: max abs err {err:.3e}")
+        assert np.isfinite(out.cpu().numpy()).all() and err <= ATOL
+
+
 @pytest.mark.parametrize("group,head_dim,block_size,dtype", [
     (1, 128, 16, "bf16"), (2, 128, 32, "bf16"), (8, 64, 16, "bf16"), (4, 64, 32, "f32"), (8, 128, 16, "f32"),
 ])

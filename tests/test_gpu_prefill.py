@@ -53,12 +53,14 @@ def test_prefill_small_workloads_match_oracle(k):
 
 @pytest.mark.parametrize("group,head_dim,block_size", [
     (1, 128, 16), (2, 128, 32), (4, 64, 16), (8, 128, 32), (8, 64, 16), (4, 128, 32),
+    (4, 128, 4), (2, 64, 8), (4, 128, 64), (8, 128, 128), (1, 64, 128),
 ])
 def test_prefill_shapes_chunks_and_ragged_tails(group, head_dim, block_size):
     hkv = 2
     ctx = [1, 63, 64, 65, 150, 200]
     chunk = [1, 63, 10, 65, 33, 129]   # whole prompts, chunks, a one-row chunk
-    w = make_prefill_custom(name="prefill-shapes", seed=7 + group, dtype="bf16", num_blocks=128,
+    nb = sum(-(-L // block_size) for L in ctx) + 8
+    w = make_prefill_custom(name="prefill-shapes", seed=7 + group, dtype="bf16", num_blocks=nb,
                             num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=head_dim,
                             block_size=block_size, context_lens=ctx, chunk_lens=chunk)
     say(f"[prefill shapes] G={group} D={head_dim} B={block_size}")
