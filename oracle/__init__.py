@@ -16,6 +16,8 @@ cites step by step with no blocking, fusion or reordering:
 * ``accounting`` -- block counts, slot usage and waste, KV byte sizes.
 * ``prefix``     -- prefix caching: chained block hashes, the table of
                     cached blocks, hits capped at the prompt minus one.
+* ``swap``       -- swap-out / swap-in of sequence groups between the GPU
+                    pool and a host pool (the copy pairs a swap needs).
 
 Citation keys used in docstrings (page title, then section):
 
@@ -33,4 +35,4 @@ against values the pages print, brute force, closed forms or invariants,
 except where a docstring says "parity unpinned".
 """
 
-from . import accounting, alloc, paged, prefix  # noqa: F401
+from . import accounting, alloc, paged, prefix, swap  # noqa: F401
