@@ -34,10 +34,13 @@ def parse():
     ap.add_argument("--decode-reps", type=int, default=50, help="timed decode-only launches for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the oracle's timed sample")
-    ap.add_argument("--skip-check", action="store_true")
+    ap.add_argument("--skip-check", action="store_true",
+                    help="time the oracle sample but do not compare it with the GPU's rows")
     ap.add_argument("--prefill", type=int, default=0, metavar="K",
                     help="instead of the decode benchmark: prefill workload K (1: 4 x 4,100-token prompts, "
                          "2: 16 x 100-token chunks over a shared 4,000-token prefix)")
+    ap.add_argument("--block-sweep", action="store_true",
+                    help="instead of the benchmark: decode of workloads 2 and 5 at block sizes 4-128")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill summary in the decode line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="instead of the benchmark: run pa_block_copy over PAIRS distinct block pairs "
@@ -69,24 +72,17 @@ def measured_traffic(workload: int, partition_size: int):
     return e.get("hbm_bytes_per_launch")
 
 
-def block_manager_timing(w, steps: int = 32, oracle_steps: int = 4):
+def block_manager_timing(w, steps: int = 32):
     """Host bookkeeping of one decode step with the native block manager (include/pa_blocks.h):
     every sequence of the workload appends one token (growth, copy-on-write check, slot), then
-    the batch's block tables are exported.  Timed beside the oracle's Python pool doing the
-    same appends."""
-    import copy
-
+    the batch's block tables are exported."""
     import paged_kv_cache_121_amd as pa
-    from oracle import alloc
     lens = w.steps[0].context_lens
     S, B = len(lens), w.block_size
     bm = pa.pa_bm_create(w.num_blocks, B, reserve_null_block=True)
     seqs = np.array([pa.pa_bm_add_sequence(bm) for _ in range(S)], dtype=np.int64)
-    pool = alloc.BlockPool(w.num_blocks, B, reserve_null_block=True)
-    oseqs = [alloc.Sequence() for _ in range(S)]
     for i, L in enumerate(lens):
         pa.pa_bm_allocate_prompt(bm, int(seqs[i]), int(L) - 1)
-        alloc.allocate_prompt(pool, oseqs[i], int(L) - 1)
     width = -(-(int(lens.max()) + steps) // B)
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -97,15 +93,9 @@ def block_manager_timing(w, steps: int = 32, oracle_steps: int = 4):
         pa.pa_bm_block_tables(bm, seqs, width)
     t_tables = (time.perf_counter() - t0) / steps
     pa.pa_bm_destroy(bm)
-    t0 = time.perf_counter()
-    for _ in range(oracle_steps):
-        for s in oseqs:
-            alloc.prepare_write(pool, s, s.num_tokens)
-    t_oracle = (time.perf_counter() - t0) / oracle_steps
     return {"sequences": S, "append_step_us": round(t_append * 1e6, 1),
             "append_ns_per_sequence": round(t_append * 1e9 / S, 1),
-            "tables_export_us": round(t_tables * 1e6, 1),
-            "oracle_append_step_us": round(t_oracle * 1e6, 1)}
+            "tables_export_us": round(t_tables * 1e6, 1)}
 
 
 def prefix_cache_timing(seed: int = 0):
@@ -160,28 +150,77 @@ def prefix_cache_timing(seed: int = 0):
             "decode_step_bookkeeping_us": round(float(np.median(t_step)) * 1e6, 1)}
 
 
-def cpu_baseline(w, n_seqs: int):
-    """The float64 oracle on a bounded sample of the same workload, one BLAS thread."""
+def cpu_baseline(w, n_seqs: int, got=None):
+    """The float64 oracle doing the step (cache write, then decode) for a bounded sample of
+    the same workload, one thread.  Each sampled sequence's blocks are gathered into a
+    private pool (the step's copy-on-write sources included), its new token written, and
+    all its query heads decoded.  With ``got`` (the GPU's output of the same step) the
+    sampled rows are compared."""
     from threadpoolctl import threadpool_limits
 
     from oracle import paged
     st = w.steps[0]
+    B = w.block_size
+    cow = dict(zip(st.cow_dst.tolist(), st.cow_src.tolist()))
     sel = list(range(min(n_seqs, w.num_seqs)))
+    dt, kv, err = 0.0, 0, 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        paged.decode_ref(w.pool, st.q[sel], w.block_tables[sel], st.context_lens[sel], float(w.scale))
-        dt = time.perf_counter() - t0
-    kv = int(st.context_lens[sel].astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        for s in sel:
+            L = int(st.context_lens[s])
+            rows = [int(b) for b in w.block_tables[s, :-(-L // B)]]
+            t0 = time.perf_counter()
+            small = np.stack([w.pool[cow.get(b, b)] for b in rows])
+            tbl = np.arange(len(rows), dtype=np.int32)[None, :]
+            mine = np.nonzero(st.write_seq == s)[0]
+            slot = paged.slot_mapping_ref(tbl, np.zeros(len(mine), dtype=np.int32), st.write_pos[mine], B)
+            small = paged.cache_write_ref(small, st.k_new[mine], st.v_new[mine], slot)
+            want = paged.decode_ref(small, st.q[s:s + 1], tbl, [L], float(w.scale))
+            dt += time.perf_counter() - t0
+            kv += L * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+            if got is not None:
+                err = max(err, float(np.abs(got[s].astype(np.float64) - want[0]).max()))
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle decode of sequences 0-{len(sel) - 1} (all {w.num_q_heads} query heads) "
-                      f"of the same workload: {kv / 1e9:.3f} GB of KV in {dt:.1f} s, one thread",
-            "seq_layers_per_s": len(sel) / dt}
+            "sample": f"float64 oracle step (cache write + decode, all {w.num_q_heads} query heads) of "
+                      f"sequences 0-{len(sel) - 1} of the same workload: {kv / 1e9:.3f} GB of KV in "
+                      f"{dt:.1f} s, one thread",
+            "seq_layers_per_s": len(sel) / dt,
+            "max_abs_err_vs_gpu": err if got is not None else None}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, check: bool = True):
+def prefill_cpu_baseline(w, got, rows: int = 12):
+    """The float64 oracle on a bounded sample of the prefill: ``rows`` query rows of the
+    first sequence, evenly spread, all heads, one thread; compared with the GPU's rows."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    n = int(w.query_start_loc[1])
+    ctx = int(w.context_lens[0])
+    nb = -(-ctx // w.block_size)
+    pick = sorted(set(np.linspace(0, n - 1, num=min(rows, n)).astype(int).tolist()))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        small = w.pool[w.block_tables[0, :nb]].copy()
+        tbl = np.arange(nb, dtype=np.int32)[None, :]
+        sl = paged.slot_mapping_ref(tbl, np.zeros(n, dtype=np.int32), w.write_pos[:n], w.block_size)
+        small = paged.cache_write_ref(small, w.k_new[:n], w.v_new[:n], sl)
+        err = 0.0
+        keys = 0
+        for i in pick:
+            want = paged.prefill_ref(small, w.q[i:i + 1], [0, 1], [ctx - n + i + 1], tbl, float(w.scale))
+            err = max(err, float(np.abs(got[i].astype(np.float64) - want[0]).max()))
+            keys += ctx - n + i + 1
+        dt = time.perf_counter() - t0
+    flops = 4 * w.head_dim * w.num_q_heads * keys
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle prefill of {len(pick)} rows of sequence 0 (all {w.num_q_heads} heads, "
+                      f"{keys} visible keys in all), one thread, {dt:.1f} s",
+            "max_abs_err_vs_gpu": err}
+
+
+def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, cpu: bool = True):
     """Time pa_prefill on prefill workload k (chunk K/V written first by pa_cache_write).
 
     Algorithmic work = the causal attention's multiply-adds: 4 * D * Hq flops
@@ -224,25 +263,95 @@ def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, check: boo
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = w.attention_flops()
     tflops = flops / (ms * 1e-3) / 1e12
-    err = None
-    if check:  # one sampled row against the oracle (the first sequence's last row)
-        from oracle import paged
-        got = out.cpu().numpy()
-        n = int(w.query_start_loc[1])
-        ctx = int(w.context_lens[0])
-        nb = -(-ctx // w.block_size)
-        small = w.pool[w.block_tables[0, :nb]].copy()
-        tbl = np.arange(nb, dtype=np.int32)[None, :]
-        sl = paged.slot_mapping_ref(tbl, np.zeros(n, dtype=np.int32), w.write_pos[:n], w.block_size)
-        small = paged.cache_write_ref(small, w.k_new[:n], w.v_new[:n], sl)
-        want = paged.prefill_ref(small, w.q[n - 1:n], [0, 1], [ctx], tbl, float(w.scale))
-        err = float(np.abs(got[n - 1].astype(np.float64) - want[0]).max())
+    base = prefill_cpu_baseline(w, out.cpu().numpy()) if cpu else None
     return {"workload": f"prefill workload {k}: {PREFILL_NAMES[k]}", "tokens": w.total_tokens,
             "flops": flops, "us": round(ms * 1e3, 1), "tflops": round(tflops, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
-            "sampled_max_abs_err": err}
+            "cpu_baseline": base,
+            "sampled_max_abs_err": base["max_abs_err_vs_gpu"] if base else None}
+
+
+def block_size_sweep(dev, workloads=(2, 5), sizes=(4, 8, 16, 32, 64, 128), reps: int = 30, warmup: int = 3):
+    """Decode time and memory waste against the block size (the pages' block-size trade-off).
+
+    Each workload keeps its context lengths and its cache memory (613,568 token slots) and is
+    stored at every block size; one cache write + decode step is warmed up, then decode alone
+    is timed with events around each launch.  Waste = slots reserved in last blocks minus
+    tokens; lookups = block-table entries the step reads."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    from workloads import make_block_size_sweep
+    rows = []
+    for k in workloads:
+        t0 = time.perf_counter()
+        ref = None
+        for w in make_block_size_sweep(k, sizes):
+            B = w.block_size
+            st = w.steps[0]
+
+            def bf(a):
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+            def i32(a):
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+            pool = pa.PagedKVPool(bf(w.pool))
+            del w.pool
+            tables, lens, q = i32(w.block_tables), i32(st.context_lens), bf(st.q)
+            slots = pa.pa_slot_mapping(pool, tables, i32(st.write_seq), i32(st.write_pos))
+            pa.pa_cache_write(pool, bf(st.k_new), bf(st.v_new), slots)
+            max_len = int(st.context_lens.max())
+            part = pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads, max_len)
+            out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            nbytes = pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, max_len, part)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+            def decode():
+                pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=max_len,
+                             partition_size=part, out=out, workspace=ws)
+
+            for _ in range(warmup):
+                decode()
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream(dev)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in ev:
+                a.record(stream)
+                decode()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            got = out.cpu().numpy()
+            if not np.isfinite(got).all():
+                print(f"[bench] NON-FINITE OUTPUT at B={B}", file=sys.stderr)
+                sys.exit(1)
+            # every block size holds the same tokens: outputs agree up to summation order
+            ref = got if ref is None else ref
+            diff = float(np.abs(got - ref).max())
+            if not diff <= 1e-4:
+                print(f"[bench] BLOCK SIZE {B} DISAGREES with B={sizes[0]}: {diff}", file=sys.stderr)
+                sys.exit(1)
+            L = st.context_lens.astype(np.int64)
+            blocks = -(-L // B)
+            kv = w.kv_bytes(0)
+            gbs = kv / (ms * 1e-3) / 1e9
+            rows.append({"workload": k, "block_size": B, "num_seqs": w.num_seqs, "context_tokens": int(L.sum()),
+                         "partition_size": part, "decode_us": round(ms * 1e3, 2), "decode_gbs": round(gbs, 1),
+                         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                         "table_lookups": int(blocks.sum()), "reserved_slots": int((blocks * B).sum()),
+                         "wasted_slots": int((blocks * B - L).sum()),
+                         "waste_pct": round(100 * float((blocks * B - L).sum()) / float((blocks * B).sum()), 3),
+                         f"max_abs_diff_vs_B{sizes[0]}": diff})
+            print(f"[bench] block-size sweep: workload {k} B={B}: {rows[-1]['decode_us']} us "
+                  f"({rows[-1]['pct_hbm_peak']} % of peak), built in {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
+            del pool, tables, lens, q, out, ws, slots, w
+            torch.cuda.empty_cache()
+            t0 = time.perf_counter()
+    return rows
 
 
 def calibrate_copy(pairs: int, dev):
@@ -281,8 +390,15 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, dev)
         return
+    if args.block_sweep:
+        rows = block_size_sweep(dev, reps=args.decode_reps)
+        print(json.dumps({"metric": "decode attention KV-read GB/s against block size", "unit": "GB/s",
+                          "n_gpus": 1, "higher_is_better": True, "dtype": "bf16 K/V and Q, fp32 accumulate",
+                          "data": "synthetic", "sweep": rows}), flush=True)
+        return
     if args.prefill:
-        r = prefill_measurement(args.prefill, dev, reps=args.steps, warmup=args.warmup)
+        r = prefill_measurement(args.prefill, dev, reps=args.steps, warmup=args.warmup,
+                                cpu=not args.no_cpu_baseline)
         if r["sampled_max_abs_err"] is not None and not r["sampled_max_abs_err"] <= 2e-3:
             print(f"[bench] PREFILL PARITY FAILURE: {r['sampled_max_abs_err']}", file=sys.stderr)
             sys.exit(1)
@@ -290,7 +406,8 @@ def main():
                           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                           "dtype": "bf16 Q/K/V, fp32 accumulate", "data": "synthetic",
                           "config": {"workload": r["workload"], "tokens": r["tokens"]}, "us": r["us"],
-                          "roofline": r["roofline"], "sampled_max_abs_err": r["sampled_max_abs_err"]}), flush=True)
+                          "roofline": r["roofline"], "cpu_baseline": r["cpu_baseline"],
+                          "sampled_max_abs_err": r["sampled_max_abs_err"]}), flush=True)
         return
     t_gen = time.perf_counter()
     w = make_config(args.workload)
@@ -362,36 +479,29 @@ def main():
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
 
-    check = None
-    if not args.skip_check:
-        from oracle import paged
-        got = out.cpu().numpy()
-        s_max = int(np.argmax(st.context_lens))
-        small_rows = [int(b) for b in w.block_tables[s_max, :-(-max_len // w.block_size)]]
-        cow = dict(zip(st.cow_dst.tolist(), st.cow_src.tolist()))  # this step's copy-on-write sources
-        small = np.stack([w.pool[cow.get(b, b)] for b in small_rows])
-        tbl = np.arange(len(small_rows), dtype=np.int32)[None, :]
-        slot = paged.slot_mapping_ref(tbl, [0], [int(st.write_pos[s_max])], w.block_size)
-        small = paged.cache_write_ref(small, st.k_new[s_max:s_max + 1], st.v_new[s_max:s_max + 1], slot)
-        want = paged.decode_one_ref(small, st.q[s_max:s_max + 1], tbl, [int(st.context_lens[s_max])], scale, 0, 0)
-        check = float(np.abs(got[s_max, 0] - want).max())
-        if not (check <= 2e-3 and np.isfinite(got).all()):
-            print(f"[bench] PARITY FAILURE: max abs err {check}", file=sys.stderr)
-            sys.exit(1)
+    got = out.cpu().numpy()
+    if not np.isfinite(got).all():
+        print("[bench] NON-FINITE DECODE OUTPUT", file=sys.stderr)
+        sys.exit(1)
 
     traffic = measured_traffic(args.workload, part)
 
-    cpu = None
+    # the oracle runs only here: timed on a bounded sample, its rows checked against the GPU's
+    cpu, check = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seqs)
+        cpu = cpu_baseline(w, args.cpu_seqs, None if args.skip_check else got)
+        check = cpu["max_abs_err_vs_gpu"]
+        if check is not None and not check <= 2e-3:
+            print(f"[bench] PARITY FAILURE: max abs err {check}", file=sys.stderr)
+            sys.exit(1)
     host_bm = block_manager_timing(w)
     host_prefix = prefix_cache_timing()
     prefill = None
     if not args.no_prefill:
         del pool, workspace, out, q
         torch.cuda.empty_cache()
-        prefill = prefill_measurement(1, dev)
-        chunked = prefill_measurement(2, dev)
+        prefill = prefill_measurement(1, dev, cpu=not args.no_cpu_baseline)
+        chunked = prefill_measurement(2, dev, cpu=False)
         # what the cache saves on the GPU: 16 requests attend 100 uncached rows each over
         # 4,100 keys instead of their whole 4,100-token prompts
         host_prefix["prefill_us_16_cached_chunks"] = chunked["us"]

@@ -130,6 +130,25 @@ int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t 
                   int32_t num_pairs, hipStream_t stream);
 
 /*
+ * Swap copies: whole blocks from one pool to another of the same geometry,
+ * either of which may live in pinned host memory (allocated with
+ * hipHostMalloc) -- the swap-out and swap-in of [VIBE] "The vLLM procedure"
+ * step 8 and [HRL] section 12.  dst->base block dst_blocks[j] receives
+ * src->base block src_blocks[j] (K and V, every head, every slot).  One
+ * kernel moves every pair, the host side over the host link, instead of one
+ * transfer per block.
+ *   src_blocks, dst_blocks : int32 [num_pairs], device memory.
+ * A pair with an id outside its pool is skipped; destinations must be
+ * distinct.  Errors (nothing is launched): pools that differ in
+ * num_kv_heads, block_size, head_dim or dtype, or a base that is neither
+ * device memory nor pinned host memory the device addresses at the same
+ * address (PA_ERR_INVALID_ARG).  The host side must stay allocated and
+ * untouched by the host until the stream reaches the copy.
+ */
+int pa_swap_blocks(const pa_pool *src, const pa_pool *dst, const int32_t *src_blocks, const int32_t *dst_blocks,
+                   int32_t num_pairs, hipStream_t stream);
+
+/*
  * Partition size (tokens) pa_decode uses when passed partition_size == 0.
  * Returns a positive multiple of the block size, or a negative pa_status.
  */

@@ -40,6 +40,9 @@ extern "C" {
 #define PA_ERR_OUT_OF_BLOCKS (-5)
 /* An unknown sequence id. */
 #define PA_ERR_NO_SEQUENCE (-6)
+/* The sequence is swapped out: only pa_bm_swap_in, pa_bm_free_sequence and
+ * the queries take it. */
+#define PA_ERR_SWAPPED (-7)
 
 typedef struct pa_block_manager pa_block_manager;
 
@@ -168,6 +171,53 @@ int64_t pa_bm_num_cached(const pa_block_manager *bm);
 
 /* 1 and the block's digest into digest_out[32] if it is in the table, else 0. */
 int pa_bm_block_digest(const pa_block_manager *bm, int32_t block, uint8_t *digest_out);
+
+/*
+ * ---- Swapping ([VIBE] "The vLLM procedure" steps 7-8: when blocks run out,
+ * all of a sequence's blocks are evicted at once, sequences sharing blocks
+ * together, and evicted blocks are copied to CPU memory and back later;
+ * [HRL] section 12 "Understanding Swap and Eviction").
+ *
+ * The manager keeps a host pool of its own (block ids 0..num_host_blocks-1,
+ * a free queue taken from the front, freed blocks to the front, a count per
+ * block).  The copies themselves are pa_swap_blocks (pa.h) over the pairs
+ * these calls return.
+ */
+
+/* Size the host pool (ids 0..n-1, all free).  Refused while any sequence is swapped out. */
+int pa_bm_set_host_pool(pa_block_manager *bm, int64_t num_host_blocks);
+
+/*
+ * Swap out the group seqs[n] (distinct sequences on the GPU).  Their tables
+ * are walked in order; the first time a GPU block is met it gets a fresh
+ * host block and one (GPU block, host block) pair is emitted, later holders
+ * in the group share that host block; then each sequence drops its GPU
+ * references, last block first (a block still held outside the group stays;
+ * a block reaching zero goes to the free queue as pa_bm_free_sequence puts
+ * it).  gpu_blocks_out / host_blocks_out need room for as many pairs as the
+ * group has distinct blocks (at most the sum of their block counts);
+ * *num_pairs_out receives the count.  All or nothing: PA_ERR_OUT_OF_BLOCKS
+ * when the host pool has fewer free blocks than the group's distinct
+ * blocks; PA_ERR_SWAPPED when a listed sequence is already out.
+ */
+int pa_bm_swap_out(pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t *gpu_blocks_out,
+                   int32_t *host_blocks_out, int32_t *num_pairs_out);
+
+/*
+ * The reverse for a group of swapped-out sequences: (host block, GPU block)
+ * pairs, GPU blocks from the free queue (all or nothing), host references
+ * dropped last block first.  Listing a sequence on the GPU is
+ * PA_ERR_INVALID_ARG.
+ */
+int pa_bm_swap_in(pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t *host_blocks_out,
+                  int32_t *gpu_blocks_out, int32_t *num_pairs_out);
+
+/* Host pool queries: free blocks, one block's count, the free queue front to back. */
+int64_t pa_bm_num_free_host(const pa_block_manager *bm);
+int32_t pa_bm_host_refcount(const pa_block_manager *bm, int32_t block);
+int64_t pa_bm_host_free_queue(const pa_block_manager *bm, int32_t *out, int64_t cap);
+/* 1 if the sequence is swapped out, 0 if on the GPU. */
+int pa_bm_sequence_on_host(const pa_block_manager *bm, int64_t seq);
 
 /* Queries: counts, one block's references, one sequence's shape, the queue. */
 int64_t pa_bm_num_free(const pa_block_manager *bm);

@@ -6,6 +6,8 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 * ``pa_slot_mapping(pool, block_tables, seq_ids, positions) -> slots``
 * ``pa_cache_write(pool, k_new, v_new, slot_mapping)``
 * ``pa_block_copy(pool, src_blocks, dst_blocks)``
+* ``pa_swap_blocks(src_pool, dst_pool, src_blocks, dst_blocks)`` between a
+  device pool and a pinned host pool (``HostKVPool``)
 * ``pa_decode(pool, q, block_tables, context_lens, ...) -> out``
 * ``pa_decode_workspace_size(...)``, ``pa_decode_partition_size(...)``
 * ``pa_prefill(pool, q, query_start_loc, context_lens, block_tables, ...) -> out``
@@ -15,7 +17,9 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
   ``pa_bm_block_tables`` and the queries (host numpy arrays in and out);
   prefix caching: ``pa_bm_hash_blocks``, ``pa_bm_lookup_prefix``,
   ``pa_bm_allocate_prompt_cached``, ``pa_bm_commit_tokens``,
-  ``pa_bm_num_cached``, ``pa_bm_block_digest``
+  ``pa_bm_num_cached``, ``pa_bm_block_digest``; swapping:
+  ``pa_bm_set_host_pool``, ``pa_bm_swap_out``, ``pa_bm_swap_in`` and the
+  host-pool queries
 
 Tensors live on a ROCm device (torch provides memory and the current
 stream).  There is no fallback: if libpa.so is missing or the device is not
@@ -30,6 +34,7 @@ import os
 import threading
 
 __all__ = [
+    "HostKVPool",
     "OutOfBlocks",
     "PaError",
     "PagedKVPool",
@@ -56,6 +61,14 @@ __all__ = [
     "pa_bm_prepare_write",
     "pa_bm_refcount",
     "pa_bm_sequence_info",
+    "pa_bm_sequence_on_host",
+    "pa_bm_set_host_pool",
+    "pa_bm_swap_in",
+    "pa_bm_swap_out",
+    "pa_bm_num_free_host",
+    "pa_bm_host_refcount",
+    "pa_bm_host_free_queue",
+    "pa_swap_blocks",
     "pa_cache_write",
     "pa_decode",
     "pa_decode_partition_size",
@@ -131,6 +144,14 @@ _SIGNATURES = {
     "pa_bm_commit_tokens": (_I32, [_VP, _I64, _VP, _I32]),
     "pa_bm_num_cached": (_I64, [_VP]),
     "pa_bm_block_digest": (_I32, [_VP, _I32, _VP]),
+    "pa_bm_set_host_pool": (_I32, [_VP, _I64]),
+    "pa_bm_swap_out": (_I32, [_VP, _VP, _I32, _VP, _VP, ctypes.POINTER(_I32)]),
+    "pa_bm_swap_in": (_I32, [_VP, _VP, _I32, _VP, _VP, ctypes.POINTER(_I32)]),
+    "pa_bm_num_free_host": (_I64, [_VP]),
+    "pa_bm_host_refcount": (_I32, [_VP, _I32]),
+    "pa_bm_host_free_queue": (_I64, [_VP, _VP, _I64]),
+    "pa_bm_sequence_on_host": (_I32, [_VP, _I64]),
+    "pa_swap_blocks": (_I32, [_POOLP, _POOLP, _VP, _VP, _I32, _VP]),
 }
 PA_ERR_OUT_OF_BLOCKS = -5
 
@@ -229,6 +250,47 @@ class PagedKVPool:
     @property
     def desc(self):
         return ctypes.byref(self._desc)
+
+
+class HostKVPool:
+    """A block pool in pinned host memory (same layout as ``PagedKVPool``), the
+    destination of swap-outs and the source of swap-ins.  The tensor must be
+    pinned (``pin_memory=True``); the library refuses pageable memory."""
+
+    def __init__(self, data):
+        torch = _torch()
+        _need(isinstance(data, torch.Tensor) and data.device.type == "cpu", "host pool must be a CPU tensor")
+        _need(data.is_pinned(), "host pool must be pinned memory (pin_memory=True)")
+        _need(data.is_contiguous() and data.dim() == 5 and data.shape[1] == 2, "host pool layout [N][2][Hkv][B][D]")
+        _need(data.dtype in (torch.float32, torch.bfloat16), "host pool dtype must be float32 or bfloat16")
+        self.data = data
+        self.num_blocks, _, self.num_kv_heads, self.block_size, self.head_dim = (int(x) for x in data.shape)
+        self.dtype_code = PA_BF16 if data.dtype == torch.bfloat16 else PA_F32
+        self._desc = pa_pool(data.data_ptr(), self.num_blocks, self.num_kv_heads, self.block_size,
+                             self.head_dim, self.dtype_code)
+
+    @classmethod
+    def empty(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype):
+        torch = _torch()
+        return cls(torch.empty((num_blocks, 2, num_kv_heads, block_size, head_dim), dtype=dtype, pin_memory=True))
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+
+def pa_swap_blocks(src, dst, src_blocks, dst_blocks) -> None:
+    """dst[dst_blocks[j]] = src[src_blocks[j]] across pools (device <-> pinned host), one launch on
+    the current stream of the device pool's device.  The block ids are device int32 tensors."""
+    torch = _torch()
+    devs = [p.data.device for p in (src, dst) if isinstance(p, PagedKVPool)]
+    _need(len(devs) >= 1, "one of the pools must be a device pool")
+    dev = devs[0]
+    _dev_tensor(src_blocks, "src_blocks", torch.int32, 1, dev)
+    _dev_tensor(dst_blocks, "dst_blocks", torch.int32, 1, dev)
+    _need(src_blocks.shape == dst_blocks.shape, "src_blocks and dst_blocks must have the same length")
+    _check(load_library().pa_swap_blocks(src.desc, dst.desc, _ptr(src_blocks), _ptr(dst_blocks),
+                                         int(src_blocks.shape[0]), _stream(src_blocks)), "pa_swap_blocks")
 
 
 def pa_slot_mapping(pool: PagedKVPool, block_tables, seq_ids, positions, out=None):
@@ -547,3 +609,63 @@ def pa_bm_block_digest(bm, block: int):
     r = load_library().pa_bm_block_digest(bm, block, buf)
     _check(min(r, 0), "pa_bm_block_digest")
     return buf.raw if r == 1 else None
+
+
+# ------------------------------------------------------------------ swapping
+
+
+def pa_bm_set_host_pool(bm, num_host_blocks: int) -> None:
+    _check(load_library().pa_bm_set_host_pool(bm, num_host_blocks), "pa_bm_set_host_pool")
+
+
+def _group_capacity(bm, seqs) -> int:
+    return sum(pa_bm_sequence_info(bm, int(s))[1] for s in seqs)
+
+
+def pa_bm_swap_out(bm, seqs):
+    """Swap out a group; returns (GPU blocks, host blocks) int32 arrays of the copy pairs."""
+    np = _np()
+    seqs = _host(seqs, "int64")
+    cap = max(1, _group_capacity(bm, seqs))
+    g, h = np.empty(cap, dtype=np.int32), np.empty(cap, dtype=np.int32)
+    k = ctypes.c_int32()
+    _check(load_library().pa_bm_swap_out(bm, seqs.ctypes.data, len(seqs), g.ctypes.data, h.ctypes.data,
+                                         ctypes.byref(k)), "pa_bm_swap_out")
+    return g[:k.value].copy(), h[:k.value].copy()
+
+
+def pa_bm_swap_in(bm, seqs):
+    """Swap in a group; returns (host blocks, GPU blocks) int32 arrays of the copy pairs."""
+    np = _np()
+    seqs = _host(seqs, "int64")
+    cap = max(1, _group_capacity(bm, seqs))
+    h, g = np.empty(cap, dtype=np.int32), np.empty(cap, dtype=np.int32)
+    k = ctypes.c_int32()
+    _check(load_library().pa_bm_swap_in(bm, seqs.ctypes.data, len(seqs), h.ctypes.data, g.ctypes.data,
+                                        ctypes.byref(k)), "pa_bm_swap_in")
+    return h[:k.value].copy(), g[:k.value].copy()
+
+
+def pa_bm_num_free_host(bm) -> int:
+    return int(load_library().pa_bm_num_free_host(bm))
+
+
+def pa_bm_host_refcount(bm, block: int) -> int:
+    r = load_library().pa_bm_host_refcount(bm, block)
+    _check(min(r, 0), "pa_bm_host_refcount")
+    return int(r)
+
+
+def pa_bm_host_free_queue(bm):
+    np = _np()
+    lib = load_library()
+    n = int(lib.pa_bm_host_free_queue(bm, None, 0))
+    out = np.empty(max(n, 1), dtype=np.int32)
+    lib.pa_bm_host_free_queue(bm, out.ctypes.data, n)
+    return out[:n].copy()
+
+
+def pa_bm_sequence_on_host(bm, seq: int) -> bool:
+    r = load_library().pa_bm_sequence_on_host(bm, seq)
+    _check(min(r, 0), "pa_bm_sequence_on_host")
+    return r == 1

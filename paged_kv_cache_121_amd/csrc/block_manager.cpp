@@ -17,6 +17,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -190,6 +191,7 @@ struct Sequence {
   std::vector<int32_t> table;   // logical block -> physical block
   std::vector<int32_t> tokens;  // committed token ids (a prefix of the positions)
   std::vector<Digest> chain;    // digest of each full block of `tokens`
+  bool on_host = false;         // swapped out: `table` holds host pool blocks
 };
 
 }  // namespace
@@ -211,6 +213,9 @@ struct pa_block_manager {
   std::vector<Digest> digest_of;
   std::vector<uint8_t> has_digest;
   std::vector<uint8_t> scratch;  // hashing buffer
+  // host pool for swapped-out sequences: its own block ids, counts and free queue
+  std::vector<int32_t> host_ref;
+  std::deque<int32_t> host_free;
 
   void push_back(int32_t b) {
     prev[b] = tail;
@@ -266,6 +271,16 @@ struct pa_block_manager {
     if (--refcount[b] == 0) {
       if (reusable || has_digest[b]) push_back(b); else push_front(b);
     }
+  }
+  // Host pool: take the front, return to the front.
+  int32_t host_allocate() {
+    const int32_t h = host_free.front();
+    host_free.pop_front();
+    host_ref[h] = 1;
+    return h;
+  }
+  void host_release(int32_t h) {
+    if (--host_ref[h] == 0) host_free.push_front(h);
   }
   // Record ids past the committed ones (the caller checked they fit in
   // num_tokens) and enter every block they complete.
@@ -363,6 +378,7 @@ int pa_bm_fork(pa_block_manager *bm, int64_t parent, int32_t num_shared_blocks, 
   if (bm == nullptr || child_out == nullptr) return PA_ERR_INVALID_ARG;
   const Sequence *p = bm->find(parent);
   if (p == nullptr) return PA_ERR_NO_SEQUENCE;
+  if (p->on_host) return PA_ERR_SWAPPED;
   const int32_t have = (int32_t)p->table.size();
   const int32_t n = num_shared_blocks < 0 ? have : std::min(num_shared_blocks, have);
   Sequence child;
@@ -382,6 +398,7 @@ int pa_bm_allocate_prompt(pa_block_manager *bm, int64_t seq, int32_t num_tokens)
   if (bm == nullptr || num_tokens < 0) return PA_ERR_INVALID_ARG;
   Sequence *s = bm->find(seq);
   if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+  if (s->on_host) return PA_ERR_SWAPPED;
   const int64_t want = ((int64_t)num_tokens + bm->block_size - 1) / bm->block_size;
   const int64_t need = std::max<int64_t>(0, want - (int64_t)s->table.size());
   if (need > bm->queue_len) return PA_ERR_OUT_OF_BLOCKS;
@@ -396,6 +413,7 @@ int pa_bm_prepare_write(pa_block_manager *bm, int64_t seq, int32_t position, int
     return PA_ERR_INVALID_ARG;
   Sequence *s = bm->find(seq);
   if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+  if (s->on_host) return PA_ERR_SWAPPED;
   if ((size_t)position < s->tokens.size()) return PA_ERR_INVALID_ARG;  // committed
   if (bm->blocks_for_write(*s, position) > bm->queue_len) return PA_ERR_OUT_OF_BLOCKS;
   bm->do_write(*s, position, slot, cow_src, cow_dst);
@@ -415,6 +433,7 @@ int pa_bm_append_tokens(pa_block_manager *bm, const int64_t *seqs, int32_t n, in
   for (int32_t i = 0; i < n; ++i) {
     ss[i] = bm->find(seqs[i]);
     if (ss[i] == nullptr) return PA_ERR_NO_SEQUENCE;
+    if (ss[i]->on_host) return PA_ERR_SWAPPED;
     if (!distinct.insert(seqs[i]).second) return PA_ERR_INVALID_ARG;
     const Sequence &s = *ss[i];
     const int64_t logical = s.num_tokens / bm->block_size;
@@ -446,7 +465,9 @@ int pa_bm_free_sequence(pa_block_manager *bm, int64_t seq, int32_t reusable) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NO_SEQUENCE;
   const std::vector<int32_t> &t = it->second.table;
-  for (auto b = t.rbegin(); b != t.rend(); ++b) bm->release(*b, reusable != 0);  // last block first
+  for (auto b = t.rbegin(); b != t.rend(); ++b) {  // last block first
+    if (it->second.on_host) bm->host_release(*b); else bm->release(*b, reusable != 0);
+  }
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -458,6 +479,7 @@ int pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seqs, int32_t 
   for (int32_t i = 0; i < n; ++i) {
     const Sequence *s = bm->find(seqs[i]);
     if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+    if (s->on_host) return PA_ERR_SWAPPED;
     if ((int64_t)s->table.size() > max_blocks_per_seq) return PA_ERR_INVALID_ARG;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -526,6 +548,7 @@ int pa_bm_allocate_prompt_cached(pa_block_manager *bm, int64_t seq, const int32_
     return PA_ERR_INVALID_ARG;
   Sequence *s = bm->find(seq);
   if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+  if (s->on_host) return PA_ERR_SWAPPED;
   if (!s->table.empty() || s->num_tokens != 0) return PA_ERR_INVALID_ARG;
   std::vector<Digest> digests;
   std::vector<int32_t> hits;
@@ -551,6 +574,7 @@ int pa_bm_commit_tokens(pa_block_manager *bm, int64_t seq, const int32_t *ids, i
   if (bm == nullptr || n < 0 || (n > 0 && ids == nullptr)) return PA_ERR_INVALID_ARG;
   Sequence *s = bm->find(seq);
   if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+  if (s->on_host) return PA_ERR_SWAPPED;
   if ((int64_t)s->tokens.size() + n > s->num_tokens) return PA_ERR_INVALID_ARG;
   bm->commit(*s, ids, n);
   return PA_OK;
@@ -563,6 +587,133 @@ int pa_bm_block_digest(const pa_block_manager *bm, int32_t block, uint8_t *diges
   if (!bm->has_digest[block]) return 0;
   std::memcpy(digest_out, bm->digest_of[block].data(), 32);
   return 1;
+}
+
+int pa_bm_set_host_pool(pa_block_manager *bm, int64_t num_host_blocks) {
+  if (bm == nullptr || num_host_blocks < 0 || num_host_blocks > INT32_MAX) return PA_ERR_INVALID_ARG;
+  for (const auto &kv : bm->seqs)
+    if (kv.second.on_host) return PA_ERR_INVALID_ARG;  // host blocks in use
+  bm->host_ref.assign(num_host_blocks, 0);
+  bm->host_free.clear();
+  for (int64_t h = 0; h < num_host_blocks; ++h) bm->host_free.push_back((int32_t)h);
+  return PA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// Validate a swap group: known, distinct, all on the given side.
+int swap_group(pa_block_manager *bm, const int64_t *seqs, int32_t n, bool on_host, std::vector<Sequence *> &ss) {
+  if (n < 0 || (n > 0 && seqs == nullptr)) return PA_ERR_INVALID_ARG;
+  ss.resize(n);
+  std::unordered_set<int64_t> distinct;
+  for (int32_t i = 0; i < n; ++i) {
+    ss[i] = bm->find(seqs[i]);
+    if (ss[i] == nullptr) return PA_ERR_NO_SEQUENCE;
+    if (!distinct.insert(seqs[i]).second) return PA_ERR_INVALID_ARG;
+    if (ss[i]->on_host != on_host) return on_host ? PA_ERR_INVALID_ARG : PA_ERR_SWAPPED;
+  }
+  return PA_OK;
+}
+
+// Move the group's tables to the other pool: the first holder of each block
+// takes a fresh block there (one copy pair), later holders share it; then each
+// sequence drops its references in the pool it left, last block first.
+template <typename Alloc, typename Share, typename Release>
+int32_t move_group(std::vector<Sequence *> &ss, Alloc alloc_dst, Share share_dst, Release release_src,
+                   int32_t *src_out, int32_t *dst_out) {
+  std::unordered_map<int32_t, int32_t> mapping;
+  std::vector<std::vector<int32_t>> tables(ss.size());
+  int32_t npairs = 0;
+  for (size_t i = 0; i < ss.size(); ++i) {
+    for (int32_t b : ss[i]->table) {
+      auto it = mapping.find(b);
+      if (it != mapping.end()) {
+        share_dst(it->second);
+        tables[i].push_back(it->second);
+      } else {
+        const int32_t d = alloc_dst();
+        mapping.emplace(b, d);
+        src_out[npairs] = b;
+        dst_out[npairs] = d;
+        ++npairs;
+        tables[i].push_back(d);
+      }
+    }
+  }
+  for (size_t i = 0; i < ss.size(); ++i) {
+    const std::vector<int32_t> &t = ss[i]->table;
+    for (auto b = t.rbegin(); b != t.rend(); ++b) release_src(*b);
+    ss[i]->table = std::move(tables[i]);
+  }
+  return npairs;
+}
+
+int64_t distinct_blocks(const std::vector<Sequence *> &ss) {
+  std::unordered_set<int32_t> d;
+  for (const Sequence *s : ss) d.insert(s->table.begin(), s->table.end());
+  return (int64_t)d.size();
+}
+}  // namespace
+
+extern "C" {
+
+int pa_bm_swap_out(pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t *gpu_blocks_out,
+                   int32_t *host_blocks_out, int32_t *num_pairs_out) {
+  if (bm == nullptr || num_pairs_out == nullptr) return PA_ERR_INVALID_ARG;
+  std::vector<Sequence *> ss;
+  const int st = swap_group(bm, seqs, n, false, ss);
+  if (st != PA_OK) return st;
+  const int64_t need = distinct_blocks(ss);
+  if (need > 0 && (gpu_blocks_out == nullptr || host_blocks_out == nullptr)) return PA_ERR_INVALID_ARG;
+  if (need > (int64_t)bm->host_free.size()) return PA_ERR_OUT_OF_BLOCKS;
+  *num_pairs_out = move_group(
+      ss, [bm] { return bm->host_allocate(); }, [bm](int32_t h) { ++bm->host_ref[h]; },
+      [bm](int32_t b) { bm->release(b, false); }, gpu_blocks_out, host_blocks_out);
+  for (Sequence *s : ss) s->on_host = true;
+  return PA_OK;
+}
+
+int pa_bm_swap_in(pa_block_manager *bm, const int64_t *seqs, int32_t n, int32_t *host_blocks_out,
+                  int32_t *gpu_blocks_out, int32_t *num_pairs_out) {
+  if (bm == nullptr || num_pairs_out == nullptr) return PA_ERR_INVALID_ARG;
+  std::vector<Sequence *> ss;
+  const int st = swap_group(bm, seqs, n, true, ss);
+  if (st != PA_OK) return st;
+  const int64_t need = distinct_blocks(ss);
+  if (need > 0 && (gpu_blocks_out == nullptr || host_blocks_out == nullptr)) return PA_ERR_INVALID_ARG;
+  if (need > bm->queue_len) return PA_ERR_OUT_OF_BLOCKS;
+  *num_pairs_out = move_group(
+      ss, [bm] { return bm->allocate(); }, [bm](int32_t b) { ++bm->refcount[b]; },
+      [bm](int32_t h) { bm->host_release(h); }, host_blocks_out, gpu_blocks_out);
+  for (Sequence *s : ss) s->on_host = false;
+  return PA_OK;
+}
+
+int64_t pa_bm_num_free_host(const pa_block_manager *bm) {
+  return bm ? (int64_t)bm->host_free.size() : PA_ERR_INVALID_ARG;
+}
+
+int pa_bm_sequence_on_host(const pa_block_manager *bm, int64_t seq) {
+  if (bm == nullptr) return PA_ERR_INVALID_ARG;
+  const Sequence *s = bm->find(seq);
+  if (s == nullptr) return PA_ERR_NO_SEQUENCE;
+  return s->on_host ? 1 : 0;
+}
+
+int32_t pa_bm_host_refcount(const pa_block_manager *bm, int32_t block) {
+  if (bm == nullptr || block < 0 || block >= (int64_t)bm->host_ref.size()) return PA_ERR_INVALID_ARG;
+  return bm->host_ref[block];
+}
+
+int64_t pa_bm_host_free_queue(const pa_block_manager *bm, int32_t *out, int64_t cap) {
+  if (bm == nullptr || (out == nullptr && cap > 0)) return PA_ERR_INVALID_ARG;
+  int64_t i = 0;
+  for (int32_t h : bm->host_free) {
+    if (i < cap) out[i] = h;
+    ++i;
+  }
+  return i;
 }
 
 int64_t pa_bm_num_free(const pa_block_manager *bm) { return bm ? bm->queue_len : PA_ERR_INVALID_ARG; }

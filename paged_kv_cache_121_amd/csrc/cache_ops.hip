@@ -58,21 +58,25 @@ cache_write_kernel(char *__restrict__ pool, int64_t num_slots, int num_kv_heads,
 }
 
 // Grid (pairs, slices): each workgroup copies one 16 KiB slice of one block,
-// four 16-byte words per lane with all loads issued before the stores.
+// four 16-byte words per lane with all loads issued before the stores.  The
+// source and destination pools may differ (a swap between device memory and
+// pinned host memory reads or writes the host side over the host link; one
+// launch keeps every pair's transfer in flight together).
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 constexpr int64_t kCopySlice = (int64_t)kCopyThreads * kCopyUnroll * 16;
 
 __global__ void __launch_bounds__(kCopyThreads)
-block_copy_kernel(char *__restrict__ pool, int64_t num_blocks, int64_t block_bytes,
-                  const int32_t *__restrict__ src_blocks, const int32_t *__restrict__ dst_blocks) {
+block_copy_kernel(const char *__restrict__ src_pool, int64_t src_num_blocks, char *__restrict__ dst_pool,
+                  int64_t dst_num_blocks, int64_t block_bytes, const int32_t *__restrict__ src_blocks,
+                  const int32_t *__restrict__ dst_blocks) {
   const int pair = blockIdx.x;
   const int64_t src = src_blocks[pair];
   const int64_t dst = dst_blocks[pair];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks) return;
   const int64_t base = (int64_t)blockIdx.y * kCopySlice;
-  const uint4 *s = reinterpret_cast<const uint4 *>(pool + src * block_bytes + base);
-  uint4 *d = reinterpret_cast<uint4 *>(pool + dst * block_bytes + base);
+  const uint4 *s = reinterpret_cast<const uint4 *>(src_pool + src * block_bytes + base);
+  uint4 *d = reinterpret_cast<uint4 *>(dst_pool + dst * block_bytes + base);
   const int64_t words = (block_bytes - base) / 16 < kCopySlice / 16 ? (block_bytes - base) / 16 : kCopySlice / 16;
   uint4 buf[kCopyUnroll];
 #pragma unroll
@@ -112,9 +116,16 @@ hipError_t launch_cache_write(const PoolDesc &pool, const void *k_new, const voi
 
 hipError_t launch_block_copy(const PoolDesc &pool, const int32_t *src, const int32_t *dst, int num_pairs,
                              hipStream_t stream) {
-  const int slices = (int)((pool.block_bytes + kCopySlice - 1) / kCopySlice);
-  hipLaunchKernelGGL(block_copy_kernel, dim3(num_pairs, slices), dim3(kCopyThreads), 0, stream, pool.base,
-                     pool.num_blocks, pool.block_bytes, src, dst);
+  return launch_swap(pool.base, pool.num_blocks, pool.base, pool.num_blocks, pool.block_bytes, src, dst, num_pairs,
+                     stream);
+}
+
+hipError_t launch_swap(const char *src_base, int64_t src_num_blocks, char *dst_base, int64_t dst_num_blocks,
+                       int64_t block_bytes, const int32_t *src, const int32_t *dst, int num_pairs,
+                       hipStream_t stream) {
+  const int slices = (int)((block_bytes + kCopySlice - 1) / kCopySlice);
+  hipLaunchKernelGGL(block_copy_kernel, dim3(num_pairs, slices), dim3(kCopyThreads), 0, stream, src_base,
+                     src_num_blocks, dst_base, dst_num_blocks, block_bytes, src, dst);
   return hipGetLastError();
 }
 

@@ -50,6 +50,27 @@ int check_pool(const pa_pool *p, PoolDesc *d) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// The address a kernel uses for a pool base: device memory as is, pinned host
+// memory (hipHostMalloc) only where the device address equals the host one.
+// Anything else -- pageable host memory, an unknown pointer -- is refused, so
+// no kernel is launched on memory the device cannot reach.
+int device_view(char *p, char **out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_INVALID_ARG;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PA_OK;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer == p) {
+    *out = p;
+    return PA_OK;
+  }
+  return PA_ERR_INVALID_ARG;
+}
+
 int partition_unit(int block_size) { return block_size < 16 ? 16 : block_size; }
 
 int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
@@ -62,7 +83,11 @@ int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int ma
   const int unit = partition_unit(block_size);
   part = (part + unit - 1) / unit * unit;
   const int64_t cap = (int64_t)kMaxPartitionBlocks * block_size / unit * unit;
-  if (part > cap) part = cap;
+  if (part > cap) {
+    // as few partitions as the cap allows, of equal length (no near-empty last one)
+    const int64_t nparts = (max_context_len + cap - 1) / cap;
+    part = ((max_context_len + nparts - 1) / nparts + unit - 1) / unit * unit;
+  }
   return (int)part;
 }
 
@@ -103,6 +128,7 @@ const char *pa_status_str(int status) {
     case PA_ERR_HIP: return "HIP launch failure";
     case PA_ERR_OUT_OF_BLOCKS: return "out of free blocks";
     case PA_ERR_NO_SEQUENCE: return "unknown sequence id";
+    case PA_ERR_SWAPPED: return "sequence is swapped out";
     default: return "unknown status";
   }
 }
@@ -141,6 +167,25 @@ int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t 
   if (num_pairs == 0) return PA_OK;
   if (src_blocks == nullptr || dst_blocks == nullptr) return PA_ERR_INVALID_ARG;
   return status_of(launch_block_copy(d, src_blocks, dst_blocks, num_pairs, stream));
+}
+
+int pa_swap_blocks(const pa_pool *src, const pa_pool *dst, const int32_t *src_blocks, const int32_t *dst_blocks,
+                   int32_t num_pairs, hipStream_t stream) {
+  PoolDesc s, d;
+  int st = check_pool(src, &s);
+  if (st != PA_OK) return st;
+  st = check_pool(dst, &d);
+  if (st != PA_OK) return st;
+  if (s.num_kv_heads != d.num_kv_heads || s.block_size != d.block_size || s.head_dim != d.head_dim ||
+      s.dtype != d.dtype)
+    return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PA_ERR_INVALID_ARG;
+  char *sv = nullptr, *dv = nullptr;
+  if (device_view(s.base, &sv) != PA_OK || device_view(d.base, &dv) != PA_OK) return PA_ERR_INVALID_ARG;
+  return status_of(launch_swap(sv, s.num_blocks, dv, d.num_blocks, s.block_bytes, src_blocks, dst_blocks, num_pairs,
+                               stream));
 }
 
 int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,

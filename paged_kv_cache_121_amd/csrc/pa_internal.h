@@ -73,6 +73,11 @@ hipError_t launch_cache_write(const PoolDesc &pool, const void *k_new, const voi
                               const int64_t *slots, int num_tokens, hipStream_t stream);
 hipError_t launch_block_copy(const PoolDesc &pool, const int32_t *src, const int32_t *dst, int num_pairs,
                              hipStream_t stream);
+// Whole-block copies from one pool to another of the same geometry (bases as
+// the device sees them; either may be pinned host memory).
+hipError_t launch_swap(const char *src_base, int64_t src_num_blocks, char *dst_base, int64_t dst_num_blocks,
+                       int64_t block_bytes, const int32_t *src, const int32_t *dst, int num_pairs,
+                       hipStream_t stream);
 // Returns hipErrorInvalidValue when no kernel is built for the shape.
 hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int block_size, int group);

@@ -64,6 +64,12 @@ def test_host_side_argument_checks_without_a_gpu():
     b4 = pa.pa_pool(0x1000, 64, 4, 4, 64, pa.PA_F32)
     assert lib.pa_decode(ref(b4), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 8, 0, None, 0, None) == -1
     assert lib.pa_decode_partition_size(ref(b4), 3, 4, 47) % 16 == 0
+    # swaps: pools must match, and a base must be device or pinned host memory (checked
+    # before anything is launched; these fake addresses are neither)
+    other = pa.pa_pool(0x2000, 8, 4, 32, 64, pa.PA_F32)
+    assert lib.pa_swap_blocks(ref(good), ref(other), 1, 1, 1, None) == -1
+    assert lib.pa_swap_blocks(ref(good), ref(good), 1, 1, 1, None) == -1
+    assert lib.pa_swap_blocks(ref(good), ref(good), None, None, 0, None) == 0
     # null pool base, negative sizes
     assert lib.pa_block_copy(ref(pa.pa_pool(None, 16, 4, 16, 64, 0)), 1, 1, 1, None) == -1
     assert lib.pa_block_copy(ref(good), 1, 1, -1, None) == -1

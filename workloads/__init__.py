@@ -13,6 +13,8 @@ from .configs import (  # noqa: F401
     PREFILL_NAMES,
     PrefillWorkload,
     TokenModel,
+    config_lengths,
+    make_block_size_sweep,
     make_prefill,
     make_prefill_custom,
     make_token_model,

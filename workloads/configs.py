@@ -234,6 +234,67 @@ def _lognormal_lengths(rng, n, median, sigma, lo, hi):
     return np.clip(np.rint(rng.lognormal(mean=np.log(median), sigma=sigma, size=n)), lo, hi).astype(np.int64)
 
 
+def _config5_lengths(small: bool):
+    """Workload 5's lognormal lengths and the seed that drew them (redrawn until they fit)."""
+    if small:
+        S, median, hi, n, steps, seed = 24, 60, 2048, 1024, 4, 105
+    else:
+        S, median, hi, n, steps, seed = 512, 600, 40960, 38348, 32, 5
+    s = seed
+    while True:
+        rng = np.random.default_rng(s)
+        lens = _lognormal_lengths(rng, S, median, 1.0, 1, hi)
+        need = sum(_blocks_for(L + steps - 1, 16) for L in lens)
+        if need <= n - 1:
+            return lens, s
+        s += 1
+
+
+def config_lengths(k: int, small: bool = False) -> np.ndarray:
+    """Context lengths of workload 2 or 5 (step 0)."""
+    if k == 2:
+        rng = np.random.default_rng((100 + k) if small else k)
+        return rng.integers(100, 165, size=6) if small else rng.integers(4100, 4165, size=64)
+    if k == 5:
+        return _config5_lengths(small)[0]
+    raise ValueError(f"no length recipe for workload {k}")
+
+
+def make_block_size_sweep(k: int, sizes):
+    """Workload 2 or 5 (one decode step) stored at each block size in ``sizes``, in turn.
+
+    The tokens' K/V, the query and the step's new K/V are drawn once (token
+    major), so every block size holds the same contents; each size keeps the
+    same cache memory (613,568 token slots re-cut into 613,568 / B blocks) and
+    places the sequences' blocks by the seeded free-list recipe.  Slots past a
+    sequence's tokens are NaN."""
+    lens = config_lengths(k).astype(np.int64)
+    S = len(lens)
+    Hq, Hkv, D = 32, 8, 128
+    rng = np.random.default_rng(3000 + k)
+    resident = lens - 1  # the step writes position L - 1
+    kv = _normal(rng, (int(resident.sum()), 2, Hkv, D), "bf16")
+    step = _decode_step(rng, lens, Hq, Hkv, D, "bf16")
+    offs = np.concatenate([[0], np.cumsum(resident)])
+    scale = np.float32(1.0) / np.sqrt(np.float32(D))
+    for B in sizes:
+        n = 613568 // B
+        prng = np.random.default_rng(4000 + 1000 * k + B)
+        free = list(prng.permutation(np.arange(1, n)))
+        free.reverse()
+        rows = [[int(free.pop()) for _ in range(_blocks_for(L, B))] for L in lens]
+        pool = _empty_pool(n, Hkv, B, D, "bf16")
+        for s in range(S):
+            nb = len(rows[s])
+            buf = np.full((nb * B, 2, Hkv, D), _BF16_NAN, dtype=np.uint16)
+            buf[:resident[s]] = kv[offs[s]:offs[s + 1]]
+            pool[rows[s]] = buf.reshape(nb, B, 2, Hkv, D).transpose(0, 2, 3, 1, 4)
+        yield Workload(name=f"cfg{k}-block-size-{B}", dtype="bf16", num_blocks=n, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, block_size=B, scale=np.float32(scale), pool=pool,
+                       block_tables=_tables_array(rows, 0), steps=[step], null_block=0,
+                       meta={"prefix_tokens": 0, "placement": "free_list"})
+
+
 def make_config(k: int, small: bool = False) -> Workload:
     """Workload ``k`` (1-5).  ``small=True`` keeps its shapes and structure at sizes
     the oracle checks in seconds (several tiles, a ragged tail)."""
@@ -243,13 +304,8 @@ def make_config(k: int, small: bool = False) -> Workload:
                            num_kv_heads=4, head_dim=64, block_size=16, lengths=[25, 47, 12],
                            placement="permutation")
     if k == 2:
-        rng = np.random.default_rng(seed)
-        if small:
-            lens = rng.integers(100, 165, size=6)
-            n = 1024
-        else:
-            lens = rng.integers(4100, 4165, size=64)
-            n = 38348
+        lens = config_lengths(2, small)
+        n = 1024 if small else 38348
         return make_custom(name="cfg2-qwen3-8b-b64" + ("-small" if small else ""), seed=seed + 1000,
                            dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
                            block_size=16, lengths=lens)
@@ -273,18 +329,8 @@ def make_config(k: int, small: bool = False) -> Workload:
                            num_blocks=n, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
                            lengths=[L] * S, placement="permutation")
     if k == 5:
-        if small:
-            S, median, hi, n, steps = 24, 60, 2048, 1024, 4
-        else:
-            S, median, hi, n, steps = 512, 600, 40960, 38348, 32
-        s = seed
-        while True:
-            rng = np.random.default_rng(s)
-            lens = _lognormal_lengths(rng, S, median, 1.0, 1, hi)
-            need = sum(_blocks_for(L + steps - 1, 16) for L in lens)
-            if need <= n - 1:
-                break
-            s += 1
+        n, steps = (1024, 4) if small else (38348, 32)
+        lens, s = _config5_lengths(small)
         return make_custom(name="cfg5-high-concurrency" + ("-small" if small else ""), seed=s + 1000,
                            dtype="bf16", num_blocks=n, num_q_heads=32, num_kv_heads=8, head_dim=128,
                            block_size=16, lengths=lens, num_steps=steps)
