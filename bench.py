@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="K",
                     help="instead of the decode benchmark: prefill workload K (1: 4 x 4,100-token prompts, "
                          "2: 16 x 100-token chunks over a shared 4,000-token prefix)")
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of the benchmark: swap copies device <-> pinned host at block sizes 4/16/128")
     ap.add_argument("--block-sweep", action="store_true",
                     help="instead of the benchmark: decode of workloads 2 and 5 at block sizes 4-128")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill summary in the decode line")
@@ -354,6 +356,73 @@ def block_size_sweep(dev, workloads=(2, 5), sizes=(4, 8, 16, 32, 64, 128), reps:
     return rows
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def swap_measurement(dev, total_mib: int = 512, sizes=(4, 16, 128), reps: int = 5, dma_blocks: int = 1024):
+    """Swap-out (device -> pinned host) and swap-in of ``total_mib`` MiB of blocks of a
+    Qwen3-8B layer (8 KV heads, D128, bf16) at several block sizes.
+
+    kernel: one pa_swap_blocks launch over every (scattered) pair.  per-block DMA: one
+    copy per block (a transfer per block, as a copy engine would be driven), timed on
+    ``dma_blocks`` blocks and scaled.  contiguous DMA: one copy of the same bytes in one
+    piece, the host link's practical ceiling."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    for B in sizes:
+        block_bytes = 2 * 8 * B * 128 * 2
+        n = total_mib * 2**20 // block_bytes
+        devpool = pa.PagedKVPool(torch.randn((2 * n, 2, 8, B, 128), device=dev).to(torch.bfloat16))
+        host = pa.HostKVPool.empty(n, 8, B, 128, torch.bfloat16)
+        g = torch.randperm(2 * n, device=dev)[:n].to(torch.int32)   # scattered device blocks
+        h = torch.randperm(n, device=dev).to(torch.int32)
+
+        def timed(fn, k=reps):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(k):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / k * 1e-3
+
+        t_out = timed(lambda: pa.pa_swap_blocks(devpool, host, g, h))
+        t_in = timed(lambda: pa.pa_swap_blocks(host, devpool, h, g))
+        ok = torch.equal(devpool.data[g.long()].view(torch.int16).cpu(), host.data[h.long().cpu()].view(torch.int16))
+        m = min(dma_blocks, n)
+        gl, hl = g[:m].tolist(), h[:m].tolist()
+
+        def per_block():
+            for i in range(m):
+                host.data[hl[i]].copy_(devpool.data[gl[i]], non_blocking=True)
+
+        t_pb = timed(per_block, 1) * n / m
+        t_contig = timed(lambda: host.data.copy_(devpool.data[:n], non_blocking=True))
+        nbytes = n * block_bytes
+        rows.append({"block_size": B, "block_bytes": block_bytes, "blocks": n, "bytes": nbytes,
+                     "kernel_out_gbs": round(nbytes / t_out / 1e9, 2), "kernel_in_gbs": round(nbytes / t_in / 1e9, 2),
+                     "per_block_dma_out_gbs": round(nbytes / t_pb / 1e9, 2),
+                     "contiguous_dma_out_gbs": round(nbytes / t_contig / 1e9, 2), "bit_exact": bool(ok)})
+        print(f"[bench] swap B={B}: kernel out {rows[-1]['kernel_out_gbs']} GB/s, in {rows[-1]['kernel_in_gbs']} "
+              f"GB/s; per-block DMA {rows[-1]['per_block_dma_out_gbs']} GB/s; contiguous "
+              f"{rows[-1]['contiguous_dma_out_gbs']} GB/s", file=sys.stderr, flush=True)
+        if not ok:
+            print(f"[bench] SWAP COPY MISMATCH at B={B}", file=sys.stderr)
+            sys.exit(1)
+        del devpool, host, g, h
+        torch.cuda.empty_cache()
+    best = max(rows, key=lambda r: r["kernel_out_gbs"])
+    return {"sweep": rows,
+            "roofline": {"bound": "pcie", "achieved": best["kernel_out_gbs"], "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(best["kernel_out_gbs"] / PCIE_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "block_copy_kernel (device -> pinned host)"}}
+
+
 def calibrate_copy(pairs: int, dev):
     """pa_block_copy of ``pairs`` distinct 64 KiB blocks (bf16, 8 KV heads, B16, D128):
     reads and writes exactly pairs * 65536 bytes per launch."""
@@ -389,6 +458,11 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, dev)
+        return
+    if args.swap:
+        r = swap_measurement(dev)
+        print(json.dumps({"metric": "swap copy GB/s (device <-> pinned host)", "unit": "GB/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "bf16 blocks", "data": "synthetic", **r}), flush=True)
         return
     if args.block_sweep:
         rows = block_size_sweep(dev, reps=args.decode_reps)
