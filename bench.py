@@ -43,6 +43,8 @@ def parse():
                     help="instead of the benchmark: swap copies device <-> pinned host at block sizes 4/16/128")
     ap.add_argument("--block-sweep", action="store_true",
                     help="instead of the benchmark: decode of workloads 2 and 5 at block sizes 4-128")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the summary of workloads 3-5 in the decode line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill summary in the decode line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="instead of the benchmark: run pa_block_copy over PAIRS distinct block pairs "
@@ -356,6 +358,99 @@ def block_size_sweep(dev, workloads=(2, 5), sizes=(4, 8, 16, 32, 64, 128), reps:
     return rows
 
 
+def d2d_copy_gbs(dev, nbytes: int = 2 << 30, reps: int = 10):
+    """A plain device-to-device copy of ``nbytes`` (torch's copy kernel): bytes read / time,
+    the practical streaming rate beside the 8 TB/s peak (each byte is also written)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "read_gbs": round(nbytes / t / 1e9, 1), "read_plus_write_gbs": round(2 * nbytes / t / 1e9, 1)}
+
+
+def other_workloads(dev, ks=(3, 4, 5), reps: int = 20):
+    """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping, cache write,
+    decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    from workloads import CONFIG_NAMES, make_config
+    out = {}
+    for k in ks:
+        t0 = time.perf_counter()
+        w = make_config(k)
+        bf = w.dtype == "bf16"
+
+        def d(a):
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if bf else np.ascontiguousarray(a))
+            return (t.view(torch.bfloat16) if bf else t).to(dev)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+        pool = pa.PagedKVPool(d(w.pool))
+        del w.pool
+        tables = i32(w.block_tables)
+        keep = bool(w.meta.get("prefix_tokens"))
+        steps = []
+        for st in w.steps:
+            steps.append((i32(st.cow_src), i32(st.cow_dst), i32(st.write_seq), i32(st.write_pos), d(st.k_new),
+                          d(st.v_new), d(st.q), i32(st.context_lens), int(st.context_lens.max()), len(st.cow_src)))
+        stream = torch.cuda.current_stream(dev)
+
+        def run(i, decode_only=False):
+            cs, cd, ws, wp, kn, vn, q, lens, mx, ncow = steps[i]
+            if not decode_only:
+                if ncow:
+                    pa.pa_block_copy(pool, cs, cd)
+                slots = pa.pa_slot_mapping(pool, tables, ws, wp)
+                pa.pa_cache_write(pool, kn, vn, slots)
+            return pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=mx, keep_cached=keep)
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(len(steps)):
+            o = run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / len(steps)
+        if not torch.isfinite(o).all():
+            print(f"[bench] NON-FINITE OUTPUT in workload {k}", file=sys.stderr)
+            sys.exit(1)
+        for _ in range(3):
+            run(0, True)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            run(0, True)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        kv = w.kv_bytes(0)
+        out[f"workload{k}"] = {"workload": CONFIG_NAMES[k], "steps": len(steps), "step_us": round(ms_step * 1e3, 2),
+                               "decode_us": round(ms * 1e3, 2), "kv_bytes": kv,
+                               "decode_gbs": round(kv / ms / 1e6, 1),
+                               "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
+                               "kv_cache_policy": "keep cached" if keep else "stream"}
+        print(f"[bench] workload {k}: decode {out[f'workload{k}']['decode_us']} us "
+              f"({out[f'workload{k}']['pct_hbm_peak']} %), step {out[f'workload{k}']['step_us']} us, "
+              f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        del pool, tables, steps, w
+        torch.cuda.empty_cache()
+    return out
+
+
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 
 
@@ -569,6 +664,8 @@ def main():
             print(f"[bench] PARITY FAILURE: max abs err {check}", file=sys.stderr)
             sys.exit(1)
     host_bm = block_manager_timing(w)
+    d2d = d2d_copy_gbs(dev)
+    others = None if args.no_other_workloads else other_workloads(dev)
     host_prefix = prefix_cache_timing()
     prefill = None
     if not args.no_prefill:
@@ -611,6 +708,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
+        "d2d_copy": d2d,
+        "other_workloads": others,
         "block_manager": host_bm,
         "prefix_cache": host_prefix,
         "prefill": prefill,

@@ -272,6 +272,11 @@ int pa_prefill(const pa_pool *pool, const void *q, float *out, const int32_t *qu
   if (!prefill_supported(d.dtype, d.head_dim, d.block_size, num_q_heads / d.num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_query_len == 0 || total_tokens == 0) return PA_OK;
+  {  // one workgroup per (row tile, KV head, sequence), in a one-dimensional grid
+    const int64_t tokens_per_tile = kPrefillRows / (num_q_heads / d.num_kv_heads);
+    const int64_t tiles = ((int64_t)max_query_len + tokens_per_tile - 1) / tokens_per_tile;
+    if (tiles * d.num_kv_heads * num_seqs > INT32_MAX - 64) return PA_ERR_UNSUPPORTED;
+  }
   if (q == nullptr || out == nullptr || query_start_loc == nullptr || context_lens == nullptr ||
       block_tables == nullptr)
     return PA_ERR_INVALID_ARG;

@@ -12,6 +12,8 @@ namespace pa {
 
 // Largest partition, in blocks, whose table entries one workgroup stages in LDS.
 constexpr int kMaxPartitionBlocks = 512;
+// Query rows (GQA head x token) one prefill workgroup takes: 16 per wave, 4 waves.
+constexpr int kPrefillRows = 64;
 
 struct PoolDesc {
   char *base;

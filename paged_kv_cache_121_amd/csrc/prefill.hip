@@ -7,29 +7,35 @@
 // row i sits at position p = context_lens[s] - n_s + i and attends causally
 // over cached positions 0 .. p, found through the block table.
 //
-// Unlike decode this is a dense contraction, so it runs on the matrix cores
-// (v_mfma_f32_16x16x32_bf16).  One workgroup of 4 waves takes 128 query rows
-// of one KV head (32 per wave, two 16-row groups sharing every K and V
-// operand read): rows are (head of the group, token) pairs, head-major, so
-// every row of the workgroup reads the same K/V.  K/V tiles of 64 keys are
-// gathered through the block table into LDS (double-buffered, the next
-// tile's global loads in flight while the current one is used), and each
-// wave computes flash-attention style on its rows:
-//   S^T = K Q^T   A = K rows from LDS (ds_read_b128, XOR-swizzled rows so 16
-//                 rows hit 16 different bank groups), B = Q^T held in
-//                 registers.  The C layout of S^T gives every lane one row
-//                 and four consecutive keys per 16-key sub-tile.
-//   P V           A = P straight from those registers: the contraction's key
-//                 order is permuted (slots 0-3 of a lane group are keys
-//                 4g..4g+3 of one sub-tile, slots 4-7 the same keys of the
-//                 next) and V's operand is built in the same order with the
-//                 LDS transpose read ds_read_b64_tr_b16 from row-major V.
-// P is split into bf16 high and low parts (two MFMAs), so rounding P costs
-// about 2^-16 relative instead of 2^-9: a row attending over two keys would
-// otherwise lose up to 2.4e-3.  Online softmax in log2 units with the
-// hardware exp2, the running max raised lazily (threshold 8) as in decode.
-// Keys past the context are written to LDS as zeros (never read from HBM),
-// so padding slots cannot leak NaN through 0 * V.
+// Unlike decode this is a dense contraction, so it runs on the matrix cores.
+// One workgroup of 4 waves takes 64 query rows of one KV head (16 per wave):
+// rows are (head of the GQA group, token) pairs, head-major, so every row of
+// the workgroup reads the same K/V.  K/V tiles of 64 keys are gathered
+// through the block table into LDS, and each wave computes flash-attention
+// style on its 16 rows:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; A = K rows from LDS (ds_read_b128,
+//                 XOR-swizzled rows so 16 rows hit 16 different bank groups),
+//                 B = Q^T held in registers.  The C layout of S^T gives every
+//                 lane one row and four consecutive keys per 16-key sub-tile.
+//   P V           v_mfma_f32_16x16x32_f16; A = P straight from those registers
+//                 (the contraction's key order is permuted: slots 0-3 of a
+//                 lane group are keys 4g..4g+3 of one sub-tile, slots 4-7 the
+//                 same keys of the next), V's operand built in the same order
+//                 with the LDS transpose read ds_read_b64_tr_b16.
+// Numerics: P is rounded to fp16 (relative 2^-11; bf16's 2^-9 could cost a
+// row over two keys more than 2e-3) and V is stored in LDS as fp16, an exact
+// conversion of bf16 for |v| < 65504 (larger values saturate).  The row sums
+// come from the matrix cores too, as P times a block of ones, so they weigh
+// exactly the rounded P the output uses.  Online softmax in log2 units with
+// the hardware exp2; the scale multiplies inside the exp2 argument (one fma)
+// and the running maximum is taken on unscaled scores, raised lazily
+// (threshold 8) as in decode.
+// Pipeline: K runs two tiles ahead of the softmax and V one, so while a wave
+// turns tile t's scores into probabilities the matrix cores already compute
+// tile t+1's scores; one barrier per tile orders the LDS reuse.  Keys past
+// the context are written to LDS as zeros (never read from HBM), so padding
+// slots cannot leak NaN through 0 * V.  Workgroups take the heaviest row
+// tiles first (causal rows late in a prompt see the most keys).
 
 #include <type_traits>
 
@@ -38,22 +44,18 @@
 namespace pa {
 namespace {
 
-#ifndef PA_PREFILL_ROW_GROUPS
-#define PA_PREFILL_ROW_GROUPS 1
-#endif
-
+constexpr int kXcds = 8;  // accelerator complex dies (each with its own L2)
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
-// 16-row groups per wave: every K or V operand read from LDS feeds RG
-// matrix-core instructions, so LDS traffic per flop falls as 1/RG.
-constexpr int kRG = PA_PREFILL_ROW_GROUPS;
-constexpr int kRows = 16 * kRG * kPfWaves;  // query rows per workgroup
-constexpr int kKeys = 64;                    // keys per LDS tile
+constexpr int kRows = kPrefillRows;  // query rows per workgroup (16 per wave)
+static_assert(kRows == 16 * kPfWaves, "16 rows per wave");
+constexpr int kKeys = 64;             // keys per LDS tile
 constexpr float kPfNegInf = -__builtin_inff();
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfRescaleThreshold = 8.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -63,7 +65,7 @@ __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Max / sum over the four 16-lane groups of the wave (lanes l, l^16, l^32,
+// Max / min over the four 16-lane groups of the wave (lanes l, l^16, l^32,
 // l^48) with the gfx950 row-swap permutes: with both operands the same value,
 // permlane16_swap yields the values of lanes (l & ~16, l | 16) and
 // permlane32_swap those of (l & ~32, l | 32) -- VALU only, no LDS round trip.
@@ -73,11 +75,11 @@ __device__ __forceinline__ float group_max(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float group_sum(float x) {
+__device__ __forceinline__ float group_min(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int D>
@@ -88,7 +90,7 @@ struct PfCfg {
   static constexpr int TILEB = kKeys * ROWB;  // bytes of one K or V tile in LDS
   static constexpr int KC = D / 32;           // 32-dim steps of QK
   static constexpr int NT = D / 16;           // 16-dim output tiles of PV
-  static constexpr int LOADS = kKeys * NCH16 / kPfThreads;  // 16-byte loads per thread per K (and V) tile
+  static constexpr int LOADS = kKeys * NCH16 / kPfThreads;  // 16-byte loads per thread per K (or V) tile
 };
 
 // LDS placement (bytes within a tile) of 16-byte chunk c of K row `key`:
@@ -113,14 +115,27 @@ __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu
 prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads, const char *__restrict__ q,
                float *__restrict__ out, const int32_t *__restrict__ query_start_loc,
                const int32_t *__restrict__ context_lens, const int32_t *__restrict__ tables,
-               int max_blocks_per_seq, int num_q_heads, int total_tokens, int max_query_len, float scale_log2) {
+               int max_blocks_per_seq, int num_q_heads, int total_tokens, int max_query_len, float scale_log2,
+               int num_row_tiles, int num_seqs) {
   using C = PfCfg<D>;
   constexpr int QT = kRows / G;  // tokens per workgroup
   __shared__ __attribute__((aligned(16))) char s_k[2][C::TILEB];
   __shared__ __attribute__((aligned(16))) char s_v[2][C::TILEB];
   __shared__ int s_poison;
 
-  const int qt = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // Work order: (sequence, KV head) pairs one after another, each pair's row
+  // tiles heaviest first (causal rows late in a prompt see the most keys).
+  // Workgroups are handed to the 8 XCDs in turn, so workgroup L runs on XCD
+  // L % 8; XCD x takes the x-th eighth of the work list in order, and the
+  // workgroups resident on one XCD at a time walk the same pair's K/V together
+  // through its own L2.
+  const int total = num_row_tiles * num_kv_heads * num_seqs;
+  const int per_xcd = (int)gridDim.x / kXcds;
+  const int w = ((int)blockIdx.x % kXcds) * per_xcd + (int)blockIdx.x / kXcds;
+  if (w >= total) return;
+  const int pair = w / num_row_tiles;
+  const int qt = num_row_tiles - 1 - (w - pair * num_row_tiles);
+  const int s = pair / num_kv_heads, h = pair - s * num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, grp = lane >> 4;
@@ -132,7 +147,6 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
                    (int64_t)q0 + n > total_tokens;
   if (!bad && qt * QT >= n) return;  // no rows of this sequence in this tile
 
-  // this lane's row in the S^T layout (row r16 of the wave's 16)
   auto row_head = [&](int r) { return r / QT; };
   auto row_token = [&](int r) { return qt * QT + r % QT; };
   const int64_t hq0 = (int64_t)h * G;
@@ -148,60 +162,63 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     return;
   }
 
-  // rows of this wave: 16*kRG consecutive rows starting at wave*16*kRG;
-  // lane (r16, grp) owns row wave*16*kRG + 16*rg + r16 of group rg
-  int my_pos[kRG];
-  bool my_active[kRG];
-  bf16x8_t qb[kRG][C::KC];
-#pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    const int r = wave * 16 * kRG + 16 * rg + r16;
+  // ---- this lane's row in the S^T layout: row wave*16 + r16; Q^T operand in registers
+  // A negative scale is applied as |scale| on -Q (an exact sign flip), so the
+  // row maximum is always taken on the largest raw score.  A zero scale is
+  // applied as the smallest normal float: every probability stays within
+  // 1e-36 of uniform, and masked keys still get exactly zero.
+  const uint32_t qsign = scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const float cs = scale_log2 == 0.0f ? 1.17549435e-38f : fabsf(scale_log2);
+  int my_pos;
+  bf16x8_t qb[C::KC];
+  {
+    const int r = wave * 16 + r16;
     const int t = row_token(r);
-    my_active[rg] = t < n;
-    my_pos[rg] = my_active[rg] ? ctx - n + t : -1;
-    // Q^T operand: lane holds Q[row][kc*32 + 8*grp .. +8] for every kc
+    my_pos = t < n ? ctx - n + t : -1;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (my_active[rg]) {
+      if (t < n) {
         const char *p = q + ((((int64_t)q0 + t) * num_q_heads + hq0 + row_head(r)) * D + kc * 32 + 8 * grp) * 2;
         v = *reinterpret_cast<const u32x4_t *>(p);
+        v ^= qsign;
       }
-      qb[rg][kc] = as_bf16x8(v);
+      qb[kc] = as_bf16x8(v);
     }
   }
 
-  // key range this workgroup needs, and per-wave bounds for skipping/masking
+  // ---- tiles: the workgroup needs keys 0 .. kv_end-1; this wave's rows stop at w_pos_max
   const int last_t = min(qt * QT + QT, n) - 1;
-  const int kv_end = ctx - n + last_t + 1;  // keys 0 .. kv_end-1
+  const int kv_end = ctx - n + last_t + 1;
   const int ntiles = (kv_end + kKeys - 1) / kKeys;
-  constexpr int WR = 16 * kRG;  // rows per wave
-  int w_tmin = QT >= WR ? (wave * WR) % QT : 0;
-  int w_tmax = QT >= WR ? w_tmin + WR - 1 : QT - 1;
+  int w_tmin = QT >= 16 ? (wave * 16) % QT : 0;
+  int w_tmax = QT >= 16 ? w_tmin + 15 : QT - 1;
   w_tmin = qt * QT + w_tmin;
   w_tmax = min(qt * QT + w_tmax, n - 1);
-  const bool wave_active = w_tmin <= w_tmax;
   const int w_pos_min = ctx - n + w_tmin;
   const int w_pos_max = ctx - n + w_tmax;
+  const int w_last_tile = w_tmin <= w_tmax ? w_pos_max / kKeys : -1;  // tiles beyond are masked for every row
 
   if (tid == 0) s_poison = 0;
 
-  // ---- global -> registers -> LDS for one tile of kKeys keys.  The tile's
-  // block ids are uniform (scalar loads, validated once); every lane then
-  // issues its K/V loads unconditionally at in-bounds addresses (keys past
-  // the sequence read block 0 and are replaced by zeros), so no load waits
-  // on a per-lane table read and no branch splits the wave.
-  // A tile spans NBT whole blocks (B <= kKeys) or a kKeys-key slice of one
-  // block (B > kKeys).
+  // ---- global -> registers -> LDS.  A tile spans NBT whole blocks (B <= 64)
+  // or a 64-key slice of one block (B > 64).  Block ids are uniform scalar
+  // loads, validated; every lane issues its loads unconditionally at
+  // in-bounds addresses.  When one load instruction's KPL keys sit in one
+  // block (KPL <= B) its block address is uniform, so only the lane's row
+  // offset is per lane.  Keys past the context (last tile only) become zeros.
   constexpr int NBT = B <= kKeys ? kKeys / B : 1;
+  constexpr int KPL = kPfThreads / C::NCH16;  // keys per load instruction
   static_assert(B % 4 == 0 && (B <= kKeys ? kKeys % B == 0 : B % kKeys == 0), "block size");
-  u32x4_t kr[C::LOADS], vr[C::LOADS];
-  bool poisoned = false;
+  const int lkey = tid / C::NCH16, lch = tid % C::NCH16;
   const int seq_blocks = (ctx + B - 1) / B;
   const char *head_base = pool + (int64_t)h * B * C::ROWB;
   const int64_t kv_half = (int64_t)num_kv_heads * B * C::ROWB;  // K tile to V tile of one block
   const int32_t *table_row = tables + (int64_t)s * max_blocks_per_seq;
-  auto load_tile = [&](int t) {
+  bool poisoned = false;
+  u32x4_t kr[C::LOADS], vr[C::LOADS];
+
+  auto load_part = [&](int t, int64_t part_off, u32x4_t (&dst)[C::LOADS]) {
     int blk[NBT];
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
@@ -214,55 +231,67 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
       blk[i] = b;
     }
+    const char *ptr[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int c = tid + i * kPfThreads;
-      const int key = c / C::NCH16, ch = c % C::NCH16;
-      int b = blk[0];
-      int row_in_block;
-      if constexpr (B <= kKeys) {
-        const int slot = key / B;  // uniform per i for D = 128 and B >= 16
+      const int key = i * KPL + lkey;
+      int b, row;
+      if constexpr (B > kKeys) {
+        b = blk[0];
+        row = (t % (B / kKeys)) * kKeys + key;
+      } else if constexpr (KPL <= B) {
+        b = blk[(i * KPL) / B];
+        row = (i * KPL) % B + lkey;
+      } else {
+        const int slot = key / B;
+        b = blk[0];
 #pragma unroll
         for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
-        row_in_block = key % B;
-      } else {
-        row_in_block = (t % (B / kKeys)) * kKeys + key;
+        row = key % B;
       }
-      const char *p = head_base + (int64_t)b * 2 * kv_half + row_in_block * C::ROWB + ch * 16;
-      const bool valid = t * kKeys + key < ctx;
-      const u32x4_t kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-      const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p + kv_half));
+      ptr[i] = head_base + (int64_t)b * 2 * kv_half + part_off + row * C::ROWB + lch * 16;
+    }
+    if ((t + 1) * kKeys <= ctx) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr[i]));
+    } else {
       const u32x4_t zero = {0u, 0u, 0u, 0u};
-      kr[i] = valid ? kv : zero;
-      vr[i] = valid ? vv : zero;
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr[i]));
+        dst[i] = t * kKeys + i * KPL + lkey < ctx ? x : zero;
+      }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](char *buf) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      *reinterpret_cast<u32x4_t *>(&buf[k_lds<D>(i * KPL + lkey, lch)]) = kr[i];
+  };
+  auto store_v = [&](char *buf) {  // as fp16
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int c = tid + i * kPfThreads;
-      const int key = c / C::NCH16, ch = c % C::NCH16;
-      *reinterpret_cast<u32x4_t *>(&s_k[buf][k_lds<D>(key, ch)]) = kr[i];
-      *reinterpret_cast<u32x4_t *>(&s_v[buf][v_lds8<D>(key, 2 * ch)]) = vr[i];
+      u32x4_t vh;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        vh[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(vr[i][w] << 16),
+                                                                        __uint_as_float(vr[i][w] & 0xffff0000u)));
+      *reinterpret_cast<u32x4_t *>(&buf[v_lds8<D>(i * KPL + lkey, 2 * lch)]) = vh;
     }
   };
 
-  // ---- per-row state: running max (log2 units), partial sum of this lane's
-  // keys, and the output tiles O[4*grp + jj][16*nt + r16] of each row group
-  float m[kRG], lpart[kRG];
-  f32x4_t o[kRG][C::NT];
+  // ---- per-row state: running max (log2 units) of this lane's S row, and
+  // the output tiles O[4*grp + jj][16*nt + r16] with their row sums
+  float m = kPfNegInf;
+  f32x4_t o[C::NT], osum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    m[rg] = kPfNegInf;
-    lpart[rg] = 0.0f;
+  for (int nt = 0; nt < C::NT; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  f16x8_t ones;
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) o[rg][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.0f;
 
-  // Per-lane LDS byte offsets of the operand reads for sub-tile 0; the
-  // sub-tile, key-step and buffer offsets are compile-time constants that
-  // fold into the instructions' immediate offsets (the swizzle term depends
-  // only on the lane because 16kt, 32ks and 16 are multiples of its period).
+  // Per-lane LDS byte offsets of the operand reads; sub-tile, key-step and
+  // buffer offsets fold into the instructions' immediate offsets.
   int k_base[C::KC];
 #pragma unroll
   for (int kc = 0; kc < C::KC; ++kc) k_base[kc] = k_lds<D>(r16, kc * 4 + grp);
@@ -270,75 +299,66 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) v_base[nt] = v_lds8<D>(4 * grp + r16 / 4, 4 * nt + (r16 & 3));
 
-  auto compute_tile = [&](int t, auto buf_tag) {
-    constexpr int buf = decltype(buf_tag)::value;
-    const int k0 = t * kKeys;
-    if (!wave_active || k0 > w_pos_max) return;  // every key of the tile is after every row
-    const char *kt_lds = s_k[buf];
-    // S^T sub-tiles: sacc[rg][kt] = K[16kt .. +16] Q_rg^T; each K operand serves every row group
-    f32x4_t sacc[kRG][4];
+  // S^T of tile t: sacc[kt] = K[16kt .. +16] Q^T (raw, unscaled)
+  auto qk = [&](const char *kt_lds, f32x4_t (&sacc)[4]) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) sacc[rg][kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
-#pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          sacc[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[kc], sacc[kt], 0, 0, 0);
       }
     }
-    const bool full = k0 + kKeys - 1 <= w_pos_min;  // no key of the tile is masked for any row
-    bf16x8_t ph[kRG][2], pl[kRG][2];
-#pragma unroll
-    for (int rg = 0; rg < kRG; ++rg) {
-      // scores of this lane's row, keys k0 + 16kt + 4grp + jj
-      float sc[4][4];
-      float mx = kPfNegInf;
+  };
+  // Softmax, first half: mask tile t's raw scores in place (diagonal tiles
+  // only), take each row's maximum and raise the running maximum, rescaling
+  // O and the row sums when it moves by more than the threshold (rare).
+  auto row_max = [&](int t, f32x4_t (&sacc)[4]) {
+    const int k0 = t * kKeys;
+    if (k0 + kKeys - 1 > w_pos_min) {  // some key of the tile lies after some row
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = k0 + 16 * kt + 4 * grp + jj;
-          float v = sacc[rg][kt][jj] * scale_log2;
-          if (!full && key > my_pos[rg]) v = kPfNegInf;
-          sc[kt][jj] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = group_max(mx);
-      const float mn = fmaxf(m[rg], mx);
-      const bool upd = mn > m[rg] + kPfRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-        const float alpha = upd ? pf_exp2(m[rg] - mn) : 1.0f;
-        if (upd) m[rg] = mn;
-        lpart[rg] *= alpha;
-        // O rows are 4*grp + jj: fetch those rows' factors
-        float ar[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) o[rg][nt][jj] *= ar[jj];
-      }
-      const float ms = m[rg] == kPfNegInf ? 0.0f : m[rg];
-      // P = exp2(s - m), split into bf16 high and low parts, in the permuted key order
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float pv = pf_exp2(sc[2 * ks + half][jj] - ms);
-            lpart[rg] += pv;
-            const __bf16 hi = (__bf16)pv;
-            ph[rg][ks][4 * half + jj] = hi;
-            pl[rg][ks][4 * half + jj] = (__bf16)(pv - (float)hi);
-          }
+        for (int jj = 0; jj < 4; ++jj)
+          if (k0 + 16 * kt + 4 * grp + jj > my_pos) sacc[kt][jj] = kPfNegInf;
     }
-    // O += P V: V operand by transpose reads, keys in the same permuted order; each serves every row group
-    const char *vt_lds = s_v[buf];
+    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
+                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+    const float mt = group_max(mx) * cs;  // this tile's row maximum, log2 units (-inf if fully masked)
+    const float mn = fmaxf(m, mt);
+    const bool upd = mn > m + kPfRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      const float alpha = upd ? pf_exp2(m - mn) : 1.0f;
+      if (upd) m = mn;
+      // O rows are 4*grp + jj: fetch those rows' factors
+      float ar[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        osum[jj] *= ar[jj];
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) o[nt][jj] *= ar[jj];
+      }
+    }
+  };
+  // Softmax, second half, and O += P V(t): P = exp2(cs * s - m) in fp16 (the
+  // permuted key order), row sums P 1 and the V products on the matrix cores.
+  auto exp_pv = [&](const f32x4_t (&sacc)[4], const char *vt_lds) {
+    const float nms = m == kPfNegInf ? 0.0f : -m;
+    f16x8_t ph[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          ph[ks][4 * half + jj] = (_Float16)pf_exp2(__builtin_fmaf(sacc[2 * ks + half][jj], cs, nms));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[ks], ones, osum, 0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
 #pragma unroll
@@ -347,68 +367,79 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
         const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
-        const bf16x8_t vb = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rg = 0; rg < kRG; ++rg) {
-          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
-          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb, o[rg][nt], 0, 0, 0);
-        }
+        const f16x8_t vb = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[ks], vb, o[nt], 0, 0, 0);
       }
     }
   };
 
-  // ---- main loop over key tiles, unrolled by two so each half uses a fixed
-  // LDS buffer (its offsets are immediates)
+  // ---- pipeline.  Prologue: K(0), V(0), K(1) in LDS; V(1), K(2) in flight; S(0) computed.
+  // Iteration t: S(t+1) from K(t+1) || softmax(t), PV(t); store K(t+2) over K(t)'s
+  // buffer and V(t+1) over V(t-1)'s; barrier; load V(t+2), K(t+3).
+  load_part(0, 0, kr);
+  load_part(0, kv_half, vr);
+  store_k(s_k[0]);
+  store_v(s_v[0]);
+  if (ntiles > 1) {
+    load_part(1, 0, kr);
+    store_k(s_k[1]);
+  }
+  __syncthreads();
+  if (ntiles > 1) load_part(1, kv_half, vr);
+  if (ntiles > 2) load_part(2, 0, kr);
+  f32x4_t sA[4], sB[4];
+  if (w_last_tile >= 0) qk(s_k[0], sA);
+
+  auto step = [&](int t, auto bt, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4]) {
+    constexpr int b = decltype(bt)::value;
+    if (t <= w_last_tile) {
+      row_max(t, s_cur);
+      // one branch-free stretch: tile t+1's scores (from a stale buffer, unused,
+      // past the last tile) beside tile t's probabilities and V products
+      qk(s_k[1 - b], s_next);
+      exp_pv(s_cur, s_v[b]);
+    }
+    if (t + 2 < ntiles) store_k(s_k[b]);
+    if (t + 1 < ntiles) store_v(s_v[1 - b]);
+    __syncthreads();
+    if (t + 2 < ntiles) load_part(t + 2, kv_half, vr);
+    if (t + 3 < ntiles) load_part(t + 3, 0, kr);
+  };
   using buf0 = std::integral_constant<int, 0>;
   using buf1 = std::integral_constant<int, 1>;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
   for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load_tile(t + 1);
-    compute_tile(t, buf0{});
-    if (t + 1 < ntiles) store_tile(1);
-    __syncthreads();
+    step(t, buf0{}, sA, sB);
     if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) load_tile(t + 2);
-    compute_tile(t + 1, buf1{});
-    if (t + 2 < ntiles) store_tile(0);
-    __syncthreads();
+    step(t + 1, buf1{}, sB, sA);
   }
   if (poisoned) s_poison = 1;
   __syncthreads();
   const bool seq_poisoned = s_poison != 0;
 
-  // ---- normalise and store: row totals, then each O row divided by its total
+  // ---- normalise and store: lane holds rows 4*grp + jj, columns 16*nt + r16
 #pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    const float lrow = group_sum(lpart[rg]);
-    const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
-    float inv_r[4];
+  for (int jj = 0; jj < 4; ++jj) {
+    const int r = wave * 16 + 4 * grp + jj;
+    const int tok = row_token(r);
+    if (tok >= n) continue;
+    const float inv = osum[jj] > 0.0f ? 1.0f / osum[jj] : 0.0f;
+    float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) inv_r[jj] = __shfl(inv, 4 * grp + jj);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = wave * 16 * kRG + 16 * rg + 4 * grp + jj;
-      const int tok = row_token(r);
-      if (tok >= n) continue;
-      float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-        dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[rg][nt][jj] * inv_r[jj];
-    }
+    for (int nt = 0; nt < C::NT; ++nt) dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[nt][jj] * inv;
   }
 }
 
 template <int D, int B, int G>
 hipError_t prefill_one(const PrefillArgs &a, hipStream_t stream) {
   constexpr int QT = kRows / G;
-  const dim3 grid((a.max_query_len + QT - 1) / QT, a.pool.num_kv_heads, a.num_seqs);
+  const int row_tiles = (a.max_query_len + QT - 1) / QT;
+  const int64_t total = (int64_t)row_tiles * a.pool.num_kv_heads * a.num_seqs;
+  const dim3 grid((unsigned)((total + kXcds - 1) / kXcds * kXcds));
   hipLaunchKernelGGL((prefill_kernel<D, B, G>), grid, dim3(kPfThreads), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.query_start_loc, a.context_lens, a.block_tables,
-                     a.max_blocks_per_seq, a.num_q_heads, a.total_tokens, a.max_query_len, a.scale * kPfLog2e);
+                     a.max_blocks_per_seq, a.num_q_heads, a.total_tokens, a.max_query_len, a.scale * kPfLog2e,
+                     row_tiles, a.num_seqs);
   return hipGetLastError();
 }
 

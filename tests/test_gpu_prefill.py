@@ -80,7 +80,11 @@ def test_prefill_single_row_chunks_agree_with_decode():
     pool, got = gpu_prefill(w)
     dec = pa.pa_decode(pool, to_dev(w.q, w.dtype), i32(w.block_tables), i32(w.context_lens), scale=float(w.scale),
                        max_context_len=300).cpu().numpy()
-    assert np.abs(got - dec).max() <= 1e-5
+    # prefill rounds P to fp16 (relative 2^-11) where decode keeps fp32; both meet the
+    # parity bar against the oracle, so they agree to within it
+    want = paged.decode_ref(oracle_pool(w), w.q, w.block_tables, w.context_lens, float(w.scale))
+    assert np.abs(dec - want).max() <= ATOL and np.abs(got - want).max() <= ATOL
+    assert np.abs(got - dec).max() <= ATOL
 
 
 def test_prefill_padding_poison_is_never_read():
