@@ -12,8 +12,10 @@ namespace pa {
 
 // Largest partition, in blocks, whose table entries one workgroup stages in LDS.
 constexpr int kMaxPartitionBlocks = 512;
-// Query rows (GQA head x token) one prefill workgroup takes: 16 per wave, 4 waves.
-constexpr int kPrefillRows = 64;
+// Query rows (GQA head x token) one prefill workgroup takes: 16 per row group,
+// two groups per wave, 4 waves.
+constexpr int kPrefillRowGroups = 2;
+constexpr int kPrefillRows = 64 * kPrefillRowGroups;
 
 struct PoolDesc {
   char *base;

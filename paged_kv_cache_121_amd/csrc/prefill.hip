@@ -8,11 +8,12 @@
 // over cached positions 0 .. p, found through the block table.
 //
 // Unlike decode this is a dense contraction, so it runs on the matrix cores.
-// One workgroup of 4 waves takes 64 query rows of one KV head (16 per wave):
-// rows are (head of the GQA group, token) pairs, head-major, so every row of
-// the workgroup reads the same K/V.  K/V tiles of 64 keys are gathered
-// through the block table into LDS, and each wave computes flash-attention
-// style on its 16 rows:
+// One workgroup of 4 waves takes 128 query rows of one KV head (32 per wave,
+// two 16-row groups sharing every K and V operand read): rows are (head of
+// the GQA group, token) pairs, head-major, so every row of the workgroup
+// reads the same K/V.  K/V tiles of 64 keys go from HBM straight into LDS
+// (global_load_lds_dwordx4, no registers on the way), double-buffered, and
+// each wave computes flash-attention style on its rows:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; A = K rows from LDS (ds_read_b128,
 //                 XOR-swizzled rows so 16 rows hit 16 different bank groups),
 //                 B = Q^T held in registers.  The C layout of S^T gives every
@@ -23,19 +24,15 @@
 //                 same keys of the next), V's operand built in the same order
 //                 with the LDS transpose read ds_read_b64_tr_b16.
 // Numerics: P is rounded to fp16 (relative 2^-11; bf16's 2^-9 could cost a
-// row over two keys more than 2e-3) and V is stored in LDS as fp16, an exact
-// conversion of bf16 for |v| < 65504 (larger values saturate).  The row sums
-// come from the matrix cores too, as P times a block of ones, so they weigh
-// exactly the rounded P the output uses.  Online softmax in log2 units with
-// the hardware exp2; the scale multiplies inside the exp2 argument (one fma)
-// and the running maximum is taken on unscaled scores, raised lazily
-// (threshold 8) as in decode.
-// Pipeline: K runs two tiles ahead of the softmax and V one, so while a wave
-// turns tile t's scores into probabilities the matrix cores already compute
-// tile t+1's scores; one barrier per tile orders the LDS reuse.  Keys past
-// the context are written to LDS as zeros (never read from HBM), so padding
-// slots cannot leak NaN through 0 * V.  Workgroups take the heaviest row
-// tiles first (causal rows late in a prompt see the most keys).
+// row over two keys more than 2e-3) and V is converted to fp16 on its way
+// into the V tile, exact for |v| < 65504 (larger values saturate).  The row
+// sums come from the matrix cores too, as P times a block of ones, so they
+// weigh exactly the rounded P the output uses.  Online softmax in log2 units
+// with the hardware exp2; the scale multiplies inside the exp2 argument (one
+// fma) and the running maximum is taken on unscaled scores, raised lazily
+// (threshold 8) as in decode.  Workgroups take each (sequence, head) pair's
+// heaviest row tiles first and each XCD takes a contiguous run of the work,
+// so the workgroups resident on one XCD share K/V in its L2.
 
 #include <type_traits>
 
@@ -47,8 +44,9 @@ namespace {
 constexpr int kXcds = 8;  // accelerator complex dies (each with its own L2)
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kRows = kPrefillRows;  // query rows per workgroup (16 per wave)
-static_assert(kRows == 16 * kPfWaves, "16 rows per wave");
+constexpr int kRG = kPrefillRowGroups;  // 16-row groups per wave
+constexpr int kRows = kPrefillRows;      // query rows per workgroup
+static_assert(kRows == 16 * kRG * kPfWaves, "16 * kRG rows per wave");
 constexpr int kKeys = 64;             // keys per LDS tile
 constexpr float kPfNegInf = -__builtin_inff();
 constexpr float kPfLog2e = 1.4426950408889634f;
@@ -121,7 +119,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   constexpr int QT = kRows / G;  // tokens per workgroup
   __shared__ __attribute__((aligned(16))) char s_k[2][C::TILEB];
   __shared__ __attribute__((aligned(16))) char s_v[2][C::TILEB];
-  __shared__ int s_poison;
+  __shared__ __attribute__((aligned(16))) char s_vst[C::TILEB];  // V as loaded (bf16), before conversion
 
   // Work order: (sequence, KV head) pairs one after another, each pair's row
   // tiles heaviest first (causal rows late in a prompt see the most keys).
@@ -147,8 +145,8 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
                    (int64_t)q0 + n > total_tokens;
   if (!bad && qt * QT >= n) return;  // no rows of this sequence in this tile
 
-  auto row_head = [&](int r) { return r / QT; };
-  auto row_token = [&](int r) { return qt * QT + r % QT; };
+  auto row_head = [&](int r) __attribute__((always_inline)) { return r / QT; };
+  auto row_token = [&](int r) __attribute__((always_inline)) { return qt * QT + r % QT; };
   const int64_t hq0 = (int64_t)h * G;
 
   if (bad) {  // NaN rows for what this tile covers, inside the output
@@ -162,19 +160,20 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     return;
   }
 
-  // ---- this lane's row in the S^T layout: row wave*16 + r16; Q^T operand in registers
+  // ---- this lane's rows in the S^T layout: row wave*16*kRG + 16*rg + r16; Q^T operands in registers
   // A negative scale is applied as |scale| on -Q (an exact sign flip), so the
   // row maximum is always taken on the largest raw score.  A zero scale is
   // applied as the smallest normal float: every probability stays within
   // 1e-36 of uniform, and masked keys still get exactly zero.
   const uint32_t qsign = scale_log2 < 0.0f ? 0x80008000u : 0u;
   const float cs = scale_log2 == 0.0f ? 1.17549435e-38f : fabsf(scale_log2);
-  int my_pos;
-  bf16x8_t qb[C::KC];
-  {
-    const int r = wave * 16 + r16;
+  int my_pos[kRG];
+  bf16x8_t qb[kRG][C::KC];
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    const int r = wave * 16 * kRG + 16 * rg + r16;
     const int t = row_token(r);
-    my_pos = t < n ? ctx - n + t : -1;
+    my_pos[rg] = t < n ? ctx - n + t : -1;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -183,7 +182,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         v = *reinterpret_cast<const u32x4_t *>(p);
         v ^= qsign;
       }
-      qb[kc] = as_bf16x8(v);
+      qb[rg][kc] = as_bf16x8(v);
     }
   }
 
@@ -191,34 +190,38 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   const int last_t = min(qt * QT + QT, n) - 1;
   const int kv_end = ctx - n + last_t + 1;
   const int ntiles = (kv_end + kKeys - 1) / kKeys;
-  int w_tmin = QT >= 16 ? (wave * 16) % QT : 0;
-  int w_tmax = QT >= 16 ? w_tmin + 15 : QT - 1;
+  constexpr int WR = 16 * kRG;  // rows per wave
+  int w_tmin = QT >= WR ? (wave * WR) % QT : 0;
+  int w_tmax = QT >= WR ? w_tmin + WR - 1 : QT - 1;
   w_tmin = qt * QT + w_tmin;
   w_tmax = min(qt * QT + w_tmax, n - 1);
   const int w_pos_min = ctx - n + w_tmin;
   const int w_pos_max = ctx - n + w_tmax;
   const int w_last_tile = w_tmin <= w_tmax ? w_pos_max / kKeys : -1;  // tiles beyond are masked for every row
 
-  if (tid == 0) s_poison = 0;
-
-  // ---- global -> registers -> LDS.  A tile spans NBT whole blocks (B <= 64)
-  // or a 64-key slice of one block (B > 64).  Block ids are uniform scalar
-  // loads, validated; every lane issues its loads unconditionally at
-  // in-bounds addresses.  When one load instruction's KPL keys sit in one
-  // block (KPL <= B) its block address is uniform, so only the lane's row
-  // offset is per lane.  Keys past the context (last tile only) become zeros.
+  // ---- global -> LDS.  A tile spans NBT whole blocks (B <= 64) or a 64-key
+  // slice of one block (B > 64).  Block ids are uniform scalar loads,
+  // validated; every wave reads all of a tile's ids, so the poison flag is the
+  // same in every wave of the workgroup.
   constexpr int NBT = B <= kKeys ? kKeys / B : 1;
-  constexpr int KPL = kPfThreads / C::NCH16;  // keys per load instruction
   static_assert(B % 4 == 0 && (B <= kKeys ? kKeys % B == 0 : B % kKeys == 0), "block size");
-  const int lkey = tid / C::NCH16, lch = tid % C::NCH16;
   const int seq_blocks = (ctx + B - 1) / B;
   const char *head_base = pool + (int64_t)h * B * C::ROWB;
   const int64_t kv_half = (int64_t)num_kv_heads * B * C::ROWB;  // K tile to V tile of one block
   const int32_t *table_row = tables + (int64_t)s * max_blocks_per_seq;
   bool poisoned = false;
-  u32x4_t kr[C::LOADS], vr[C::LOADS];
 
-  auto load_part = [&](int t, int64_t part_off, u32x4_t (&dst)[C::LOADS]) {
+  // K and V go straight from global memory into LDS (global_load_lds_dwordx4:
+  // each instruction writes 1 KiB, lane l's 16 bytes at l * 16).  Instruction i
+  // of wave w fills tile rows RPI*(4i+w) .. +RPI-1; lane l writes slot l % NCH16
+  // of row RPI*(4i+w) + l / NCH16.  For K it loads the chunk the XOR swizzle
+  // puts in that slot; V lands unswizzled in a staging tile and is converted
+  // to fp16 into its swizzled tile by the same lane (convert_v).  Keys past the
+  // context load the last real key instead (finite; their scores are masked
+  // and their probabilities are exactly 0), so no zero fill is needed.
+  constexpr int RPI = 1024 / C::ROWB;  // key rows per instruction
+  const int dl_row = lane / C::NCH16, dl_slot = lane % C::NCH16;
+  auto load_lds = [&](int t, int64_t part_off, bool swizzle, char *buf) __attribute__((always_inline)) {
     int blk[NBT];
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
@@ -231,61 +234,58 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
       blk[i] = b;
     }
-    const char *ptr[C::LOADS];
+    const int last_row = ctx - 1 - t * kKeys;  // rows past it are past the context
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int key = i * KPL + lkey;
-      int b, row;
+      const int row = RPI * (kPfWaves * i + wave) + dl_row;
+      const int chunk = swizzle ? dl_slot ^ (row % C::NCH16) : dl_slot;
+      const int src_row = min(row, last_row);
+      int b, rib;
       if constexpr (B > kKeys) {
         b = blk[0];
-        row = (t % (B / kKeys)) * kKeys + key;
-      } else if constexpr (KPL <= B) {
-        b = blk[(i * KPL) / B];
-        row = (i * KPL) % B + lkey;
+        rib = (t % (B / kKeys)) * kKeys + src_row;
       } else {
-        const int slot = key / B;
+        const int slot = src_row / B;
         b = blk[0];
 #pragma unroll
         for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
-        row = key % B;
+        rib = src_row % B;
       }
-      ptr[i] = head_base + (int64_t)b * 2 * kv_half + part_off + row * C::ROWB + lch * 16;
-    }
-    if ((t + 1) * kKeys <= ctx) {
-#pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr[i]));
-    } else {
-      const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) {
-        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr[i]));
-        dst[i] = t * kKeys + i * KPL + lkey < ctx ? x : zero;
-      }
+      const char *src = head_base + (int64_t)b * 2 * kv_half + part_off + rib * C::ROWB + chunk * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                       (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
+                                       16, 0, 0);
     }
   };
-  auto store_k = [&](char *buf) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      *reinterpret_cast<u32x4_t *>(&buf[k_lds<D>(i * KPL + lkey, lch)]) = kr[i];
-  };
-  auto store_v = [&](char *buf) {  // as fp16
+  // V from the staging tile (this lane's own loads) to fp16 in its swizzled tile;
+  // exact for |v| < 65504 (bf16 keeps 8 significant bits, fp16 11)
+  auto convert_v = [&](char *buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
+      const int row = RPI * (kPfWaves * i + wave) + dl_row;
+      const u32x4_t x = *reinterpret_cast<const u32x4_t *>(&s_vst[(kPfWaves * i + wave) * 1024 + lane * 16]);
       u32x4_t vh;
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        vh[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(vr[i][w] << 16),
-                                                                        __uint_as_float(vr[i][w] & 0xffff0000u)));
-      *reinterpret_cast<u32x4_t *>(&buf[v_lds8<D>(i * KPL + lkey, 2 * lch)]) = vh;
+        vh[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x[w] << 16),
+                                                                        __uint_as_float(x[w] & 0xffff0000u)));
+      *reinterpret_cast<u32x4_t *>(&buf[v_lds8<D>(row, 2 * dl_slot)]) = vh;
     }
   };
+  // The LDS writes of this wave's loads are done (a barrier after this publishes them).
+  auto wait_lds_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- per-row state: running max (log2 units) of this lane's S row, and
   // the output tiles O[4*grp + jj][16*nt + r16] with their row sums
-  float m = kPfNegInf;
-  f32x4_t o[C::NT], osum = {0.0f, 0.0f, 0.0f, 0.0f};
+  float m[kRG];
+  f32x4_t o[kRG][C::NT], osum[kRG];
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rg = 0; rg < kRG; ++rg) {
+    m[rg] = kPfNegInf;
+    osum[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) o[rg][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   f16x8_t ones;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.0f;
@@ -299,66 +299,76 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) v_base[nt] = v_lds8<D>(4 * grp + r16 / 4, 4 * nt + (r16 & 3));
 
-  // S^T of tile t: sacc[kt] = K[16kt .. +16] Q^T (raw, unscaled)
-  auto qk = [&](const char *kt_lds, f32x4_t (&sacc)[4]) {
+  // S^T of tile t: sacc[rg][kt] = K[16kt .. +16] Q_rg^T (raw, unscaled); each K operand serves every row group
+  auto qk = [&](const char *kt_lds, f32x4_t (&sacc)[kRG][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) sacc[rg][kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[kc], sacc[kt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          sacc[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
       }
     }
   };
   // Softmax, first half: mask tile t's raw scores in place (diagonal tiles
   // only), take each row's maximum and raise the running maximum, rescaling
   // O and the row sums when it moves by more than the threshold (rare).
-  auto row_max = [&](int t, f32x4_t (&sacc)[4]) {
+  auto row_max = [&](int t, f32x4_t (&sacc)[kRG][4]) __attribute__((always_inline)) {
     const int k0 = t * kKeys;
-    if (k0 + kKeys - 1 > w_pos_min) {  // some key of the tile lies after some row
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      if (k0 + kKeys - 1 > w_pos_min) {  // some key of the tile lies after some row
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (k0 + 16 * kt + 4 * grp + jj > my_pos[rg]) sacc[rg][kt][jj] = kPfNegInf;
+      }
+      float mx = kPfNegInf;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[rg][kt][0], sacc[rg][kt][1]), fmaxf(sacc[rg][kt][2], sacc[rg][kt][3])));
+      const float mt = group_max(mx) * cs;  // this tile's row maximum, log2 units (-inf if fully masked)
+      const float mn = fmaxf(m[rg], mt);
+      const bool upd = mn > m[rg] + kPfRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        const float alpha = upd ? pf_exp2(m[rg] - mn) : 1.0f;
+        if (upd) m[rg] = mn;
+        // O rows are 4*grp + jj: fetch those rows' factors
+        float ar[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (k0 + 16 * kt + 4 * grp + jj > my_pos) sacc[kt][jj] = kPfNegInf;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
-                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
-    const float mt = group_max(mx) * cs;  // this tile's row maximum, log2 units (-inf if fully masked)
-    const float mn = fmaxf(m, mt);
-    const bool upd = mn > m + kPfRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-      const float alpha = upd ? pf_exp2(m - mn) : 1.0f;
-      if (upd) m = mn;
-      // O rows are 4*grp + jj: fetch those rows' factors
-      float ar[4];
+        for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ar[jj] = __shfl(alpha, 4 * grp + jj);
+        for (int jj = 0; jj < 4; ++jj) {
+          osum[rg][jj] *= ar[jj];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        osum[jj] *= ar[jj];
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) o[nt][jj] *= ar[jj];
+          for (int nt = 0; nt < C::NT; ++nt) o[rg][nt][jj] *= ar[jj];
+        }
       }
     }
   };
   // Softmax, second half, and O += P V(t): P = exp2(cs * s - m) in fp16 (the
   // permuted key order), row sums P 1 and the V products on the matrix cores.
-  auto exp_pv = [&](const f32x4_t (&sacc)[4], const char *vt_lds) {
-    const float nms = m == kPfNegInf ? 0.0f : -m;
-    f16x8_t ph[2];
+  auto exp_pv = [&](const f32x4_t (&sacc)[kRG][4], const char *vt_lds) __attribute__((always_inline)) {
+    f16x8_t ph[kRG][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int rg = 0; rg < kRG; ++rg) {
+      const float nms = m[rg] == kPfNegInf ? 0.0f : -m[rg];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          ph[ks][4 * half + jj] = (_Float16)pf_exp2(__builtin_fmaf(sacc[2 * ks + half][jj], cs, nms));
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[ks], ones, osum, 0, 0, 0);
+          for (int jj = 0; jj < 4; ++jj)
+            ph[rg][ks][4 * half + jj] = (_Float16)pf_exp2(__builtin_fmaf(sacc[rg][2 * ks + half][jj], cs, nms));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
+    }
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
 #pragma unroll
@@ -368,64 +378,65 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
         const f16x8_t vb = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[ks], vb, o[nt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
       }
     }
   };
 
-  // ---- pipeline.  Prologue: K(0), V(0), K(1) in LDS; V(1), K(2) in flight; S(0) computed.
-  // Iteration t: S(t+1) from K(t+1) || softmax(t), PV(t); store K(t+2) over K(t)'s
-  // buffer and V(t+1) over V(t-1)'s; barrier; load V(t+2), K(t+3).
-  load_part(0, 0, kr);
-  load_part(0, kv_half, vr);
-  store_k(s_k[0]);
-  store_v(s_v[0]);
-  if (ntiles > 1) {
-    load_part(1, 0, kr);
-    store_k(s_k[1]);
-  }
-  __syncthreads();
-  if (ntiles > 1) load_part(1, kv_half, vr);
-  if (ntiles > 2) load_part(2, 0, kr);
-  f32x4_t sA[4], sB[4];
-  if (w_last_tile >= 0) qk(s_k[0], sA);
-
-  auto step = [&](int t, auto bt, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4]) {
-    constexpr int b = decltype(bt)::value;
-    if (t <= w_last_tile) {
-      row_max(t, s_cur);
-      // one branch-free stretch: tile t+1's scores (from a stale buffer, unused,
-      // past the last tile) beside tile t's probabilities and V products
-      qk(s_k[1 - b], s_next);
-      exp_pv(s_cur, s_v[b]);
-    }
-    if (t + 2 < ntiles) store_k(s_k[b]);
-    if (t + 1 < ntiles) store_v(s_v[1 - b]);
-    __syncthreads();
-    if (t + 2 < ntiles) load_part(t + 2, kv_half, vr);
-    if (t + 3 < ntiles) load_part(t + 3, 0, kr);
-  };
   using buf0 = std::integral_constant<int, 0>;
   using buf1 = std::integral_constant<int, 1>;
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, buf0{}, sA, sB);
-    if (t + 1 >= ntiles) break;
-    step(t + 1, buf1{}, sB, sA);
-  }
-  if (poisoned) s_poison = 1;
+  // ---- double buffering.  Iteration t: S(t), softmax(t), PV(t) from buffer t%2;
+  // K(t+1) has been arriving in tile t-1's K buffer; convert V(t+1) from the
+  // staging tile into tile t-1's V buffer; barrier; start K(t+2) into tile t's
+  // K buffer and V(t+2) into the staging tile.
+  load_lds(0, 0, true, s_k[0]);
+  load_lds(0, kv_half, false, s_vst);
+  wait_lds_loads();
+  convert_v(s_v[0]);
   __syncthreads();
-  const bool seq_poisoned = s_poison != 0;
+  if (ntiles > 1) {
+    load_lds(1, 0, true, s_k[1]);
+    load_lds(1, kv_half, false, s_vst);
+  }
+  f32x4_t sc[kRG][4];
+  auto step = [&](int t, auto bt) __attribute__((always_inline)) {
+    constexpr int b = decltype(bt)::value;
+    if (t <= w_last_tile) {
+      qk(s_k[b], sc);
+      row_max(t, sc);
+      exp_pv(sc, s_v[b]);
+    }
+    wait_lds_loads();  // K(t+1) has arrived in s_k[1 - b], V(t+1) in the staging tile
+    if (t + 1 < ntiles) convert_v(s_v[1 - b]);
+    __syncthreads();
+    if (t + 2 < ntiles) {
+      load_lds(t + 2, 0, true, s_k[b]);
+      load_lds(t + 2, kv_half, false, s_vst);
+    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, buf0{});
+    if (t + 1 >= ntiles) break;
+    step(t + 1, buf1{});
+  }
+  const bool seq_poisoned = poisoned;
 
-  // ---- normalise and store: lane holds rows 4*grp + jj, columns 16*nt + r16
+  // ---- normalise and store: lane holds rows 4*grp + jj of each group, columns 16*nt + r16
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int r = wave * 16 + 4 * grp + jj;
-    const int tok = row_token(r);
-    if (tok >= n) continue;
-    const float inv = osum[jj] > 0.0f ? 1.0f / osum[jj] : 0.0f;
-    float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
+  for (int rg = 0; rg < kRG; ++rg) {
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[nt][jj] * inv;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = wave * 16 * kRG + 16 * rg + 4 * grp + jj;
+      const int tok = row_token(r);
+      if (tok >= n) continue;
+      const float inv = osum[rg][jj] > 0.0f ? 1.0f / osum[rg][jj] : 0.0f;
+      float *dst = out + (((int64_t)q0 + tok) * num_q_heads + hq0 + row_head(r)) * D + r16;
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        dst[16 * nt] = seq_poisoned ? __builtin_nanf("") : o[rg][nt][jj] * inv;
+    }
   }
 }
 
