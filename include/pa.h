@@ -187,6 +187,8 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
  * never do).  A call launches one kernel, plus a small combine kernel when
  * some sequence spans more than one partition.  Query head hq reads KV head
  * hq / (num_q_heads / num_kv_heads); the group size must be 1, 2, 4 or 8.
+ * At most 65,535 sequences, and (num_seqs * num_kv_heads + 8) * partitions
+ * below 2^31 (PA_ERR_UNSUPPORTED otherwise).
  * Output rows of a sequence with a context length of 0 are zero; rows of a
  * sequence whose context length is negative, exceeds max_context_len or its
  * table row, or whose table holds an id outside [0, num_blocks) among its

@@ -6,7 +6,9 @@
 // lives in physical block table[s][t / B] at offset t % B.
 //
 // Work decomposition
-//   grid (partition p, KV head h, sequence s); one workgroup of kWaves
+//   one workgroup per (partition p, KV head h, sequence s), in a
+//   one-dimensional grid ordered so each XCD gets an equal share of the
+//   (sequence, head) pairs.  A workgroup of kWaves
 //   wavefronts serves all G = Hq / Hkv query heads of KV head h, so each K/V
 //   byte is read from HBM once per step.  The workgroup owns the blocks
 //   [p * part, (p + 1) * part) of the sequence; wave w takes the workgroup's
@@ -52,13 +54,13 @@ namespace {
 #define PA_DECODE_PREFETCH 1
 #endif
 
+constexpr int kXcds = 8;  // XCDs of the chip; workgroup L is dispatched to XCD L % 8
 constexpr int kWaves = 4;
 // Chunks in flight ahead of the one being processed.  Measured on the
 // Qwen3-8B batch-64 layer: 1 ahead already hides the latency (2 ahead was
 // 3 % slower, it costs 20 more VGPRs).
 constexpr int kPrefetch = PA_DECODE_PREFETCH;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 16;                    // tokens per pipeline stage
 constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -216,7 +218,7 @@ __device__ __forceinline__ int partitions_of(int L, int max_context_len, int max
   return (L + part_tokens - 1) / part_tokens;
 }
 
-template <typename T, int D, int B, int G>
+template <typename T, int D, int B, int G, int CH>
 struct Cfg {
   static constexpr int kElem = std::is_same_v<T, float> ? 4 : 2;
   static constexpr int EPL = D / 16;             // elements per lane per token
@@ -224,15 +226,16 @@ struct Cfg {
   static constexpr int NW = VEC / 4;             // 32-bit words per lane per token
   static constexpr int QS = G < 4 ? G : 4;       // quad lanes that own distinct heads
   static constexpr int HPL = G / QS;             // heads owned per lane
-  // A pipeline stage is kChunk consecutive tokens.  Large blocks hold CPB
+  // A pipeline stage is CH consecutive tokens (STEPS load steps of 4).  Large blocks hold CPB
   // stages; small blocks (B = 4, 8) are grouped R to a stage.  A "unit" is
   // the span a wave takes at a time: one block, or R consecutive blocks.
-  static constexpr int R = B < kChunk ? kChunk / B : 1;    // blocks per unit
-  static constexpr int CPB = B < kChunk ? 1 : B / kChunk;  // pipeline stages per unit
+  static constexpr int STEPS = CH / 4;
+  static constexpr int R = B < CH ? CH / B : 1;    // blocks per unit
+  static constexpr int CPB = B < CH ? 1 : B / CH;  // pipeline stages per unit
   static constexpr int UNIT = R * B;                       // tokens per unit
   static constexpr int64_t ROW = (int64_t)D * kElem;
   static constexpr int64_t TILE = (int64_t)B * ROW;
-  static constexpr int64_t CHUNK = (int64_t)kChunk * ROW;
+  static constexpr int64_t CHUNK = (int64_t)CH * ROW;
   static constexpr int64_t STEP = 64 * VEC;      // bytes per load step (4 tokens)
 };
 
@@ -241,16 +244,17 @@ struct Cfg {
 // the Qwen3-8B batch-64 layer it raised decode bandwidth from 5.8 to 6.4
 // TB/s.  Batches whose sequences share blocks want the normal policy instead
 // (the later readers of a shared block hit in L2).
-template <typename T, int D, int B, int G, bool NT>
+template <typename T, int D, int B, int G, int CH, bool NT>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
               int max_blocks_per_seq, const int32_t *__restrict__ context_lens, int num_q_heads,
-              float scale_log2, int max_context_len, int part_blocks, int max_parts,
+              float scale_log2, int max_context_len, int part_blocks, int max_parts, int num_pairs,
               float *__restrict__ ws_o, float *__restrict__ ws_ml) {
-  using C = Cfg<T, D, B, G>;
+  using C = Cfg<T, D, B, G, CH>;
   constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB, R = C::R;
-  static_assert(B % 4 == 0 && (B < kChunk ? kChunk % B == 0 : B % kChunk == 0), "block size");
+  constexpr int NS = C::STEPS;
+  static_assert(B % 4 == 0 && (B < CH ? CH % B == 0 : B % CH == 0), "block size");
 
   __shared__ int s_tbl[kMaxPartitionBlocks];
   __shared__ float s_o[kWaves][G][D];
@@ -258,7 +262,19 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   __shared__ float s_l[kWaves][G];
   __shared__ int s_poison;
 
-  const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // One-dimensional grid.  Workgroup wg runs on XCD wg % kXcds; XCD x takes
+  // the (sequence, KV head) pairs x, x + kXcds, ..., first partition 0 of
+  // each, then partition 1 of each, and so on.  In a batch of mixed lengths
+  // most pairs have one partition, so the workgroups that exit at once all
+  // sit at the end of the dispatch order instead of in a regular pattern
+  // among the working ones (measured: with the partition index fastest, an
+  // even partition count crowded the work onto a fraction of the compute
+  // units, up to 2.7x slower).
+  const int wg = blockIdx.x, xcd = wg % kXcds, j = wg / kXcds;
+  const int per_xcd = (num_pairs + kXcds - 1) / kXcds;
+  const int pair = (j % per_xcd) * kXcds + xcd, p = j / per_xcd;
+  if (pair >= num_pairs) return;
+  const int h = pair % num_kv_heads, s = pair / num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int row = lane >> 4, col = lane & 15;
@@ -319,37 +335,37 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   const int64_t v_off = (int64_t)num_kv_heads * C::TILE;
   const int lane_off = lane * C::VEC;
 
-  auto issue = [&](int ci, Frag<NW> (&kf)[4], Frag<NW> (&vf)[4]) {
+  auto issue = [&](int ci, Frag<NW> (&kf)[NS], Frag<NW> (&vf)[NS]) {
     const int unit = wave + (ci / CPB) * kWaves;
     if constexpr (R == 1) {
       const int sub = ci % CPB;
       const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
       const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp + j * C::STEP);
+      for (int j = 0; j < NS; ++j) load_frag<NW, NT>(kf[j], kp + j * C::STEP);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp + v_off + j * C::STEP);
+      for (int j = 0; j < NS; ++j) load_frag<NW, NT>(vf[j], kp + v_off + j * C::STEP);
     } else {
       // load step j (4 tokens) lies in block 4j / B of the unit, at row 4j % B
-      const char *kp[4];
+      const char *kp[NS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NS; ++j) {
         const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit * R + (4 * j) / B]);
         kp[j] = kv_head_base + (int64_t)phys * (2 * v_off) + ((4 * j) % B) * C::ROW + lane_off;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(kf[j], kp[j]);
+      for (int j = 0; j < NS; ++j) load_frag<NW, NT>(kf[j], kp[j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_frag<NW, NT>(vf[j], kp[j] + v_off);
+      for (int j = 0; j < NS; ++j) load_frag<NW, NT>(vf[j], kp[j] + v_off);
     }
   };
-  auto process = [&](int ci, const Frag<NW> (&kf)[4], const Frag<NW> (&vf)[4]) {
-    const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * kChunk;
-    const bool partial = tok0 + kChunk > L;
+  auto process = [&](int ci, const Frag<NW> (&kf)[NS], const Frag<NW> (&vf)[NS]) {
+    const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
+    const bool partial = tok0 + CH > L;
     // QK for the 4 tokens this row sees in the chunk
-    float sc[4][HPL];
+    float sc[NS][HPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
       float a[G];
 #pragma unroll
       for (int r = 0; r < G; ++r) a[r] = partial_dot<T, NW>(qf[r], kf[j]);
@@ -364,7 +380,9 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     bool any_upd = false;
 #pragma unroll
     for (int t = 0; t < HPL; ++t) {
-      const float cm = fmaxf(fmaxf(sc[0][t], sc[1][t]), fmaxf(sc[2][t], sc[3][t]));
+      float cm = sc[0][t];
+#pragma unroll
+      for (int j = 1; j < NS; ++j) cm = fmaxf(cm, sc[j][t]);
       const float mn = fmaxf(m[t], cm);
       upd[t] = mn > m[t] + kRescaleThreshold;
       m_new[t] = upd[t] ? mn : m[t];
@@ -385,17 +403,20 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
         for (int e = 0; e < EPL; ++e) o[hh][e] *= a;
       }
     }
-    float pr[4][HPL];
+    float pr[NS][HPL];
 #pragma unroll
     for (int t = 0; t < HPL; ++t) {
       const float ms = m[t] == kNegInf ? 0.0f : m[t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pr[j][t] = fast_exp2(sc[j][t] - ms);
-      lsum[t] += (pr[0][t] + pr[1][t]) + (pr[2][t] + pr[3][t]);
+      for (int j = 0; j < NS; ++j) pr[j][t] = fast_exp2(sc[j][t] - ms);
+      float ps = pr[0][t];
+#pragma unroll
+      for (int j = 1; j < NS; ++j) ps += pr[j][t];
+      lsum[t] += ps;
     }
     // PV
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
       float v[EPL];
       widen<T, NW, EPL>(vf[j], v);
       if (partial && !(tok0 + 4 * j + row < L)) {
@@ -418,7 +439,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // process() waits for its own chunk while the next one is in flight.
   if constexpr (kPrefetch == 1) {
     if (nch > 0) {
-      Frag<NW> kA[4], vA[4], kB[4], vB[4];
+      Frag<NW> kA[NS], vA[NS], kB[NS], vB[NS];
       const int last = nch - 1;
       issue(0, kA, vA);
       int ci = 0;
@@ -434,7 +455,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     static_assert(kPrefetch == 2, "prefetch depth 1 or 2");
     // three buffers, two chunks in flight while one is processed
     if (nch > 0) {
-      Frag<NW> kA[4], vA[4], kB[4], vB[4], kC[4], vC[4];
+      Frag<NW> kA[NS], vA[NS], kB[NS], vB[NS], kC[NS], vC[NS];
       const int last = nch - 1;
       issue(0, kA, vA);
       issue(min(1, last), kB, vB);
@@ -549,13 +570,19 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
 
 template <typename T, int D, int B, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
-  const dim3 grid(a.num_partitions, a.pool.num_kv_heads, a.num_seqs);
-  auto kernel = a.stream_loads ? decode_kernel<T, D, B, G, true> : decode_kernel<T, D, B, G, false>;
+  const int pairs = a.num_seqs * a.pool.num_kv_heads;
+  const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds) * kXcds * a.num_partitions);
+  // Pipeline stage: 4 tokens for groups up to 4 (less in flight per wave,
+  // and short contexts reach their first score sooner: up to 27 % faster on
+  // 128-token contexts, the same on long ones); 16 for groups of 8, whose
+  // larger per-token arithmetic wants the longer stages on long contexts.
+  constexpr int CH = G <= 4 ? 4 : 16;
+  auto kernel = a.stream_loads ? decode_kernel<T, D, B, G, CH, true> : decode_kernel<T, D, B, G, CH, false>;
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,
-                     a.num_partitions, a.ws_o, a.ws_ml);
+                     a.num_partitions, pairs, a.ws_o, a.ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a.ws_o, a.ws_ml,

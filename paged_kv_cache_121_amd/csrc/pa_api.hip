@@ -231,6 +231,8 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
   const int part = resolve_partition(d, num_seqs, max_context_len, partition_size);
   if (part < 0) return part;
   const int parts = max_context_len == 0 ? 1 : (max_context_len + part - 1) / part;
+  // one workgroup per (pair, partition), pairs rounded up to a multiple of 8
+  if (((int64_t)num_seqs * d.num_kv_heads + 8) * parts > INT32_MAX) return PA_ERR_UNSUPPORTED;
 
   DecodeArgs a{};
   a.pool = d;

@@ -85,6 +85,10 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, float("nan"), 48, 0, 0, None, 0, None) == -1
     assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 4, 0.1, 48, 0, 2, None, 0, None) == -1  # unknown flag
     assert lib.pa_decode(ref(good), 1, 1, 1, 64, 1, 3, 4, 0.1, 1024, 16, 0, None, 0, None) == -3
+    # the grid, (sequence, KV head) pairs rounded up to 8 times partitions, must fit in int32
+    big = pa.pa_pool(0x1000, 16, 4096, 16, 64, pa.PA_F32)
+    assert lib.pa_decode(ref(big), 1, 1, 1, 65536, 1, 65535, 4096, 0.1, 1 << 20, 8192, 0, None, 0, None) == -2
+    assert lib.pa_decode(ref(big), 1, 1, 1, 65536, 1, 4, 4096, 0.1, 1 << 20, 8192, 0, None, 0, None) == -3
     # prefill: bf16 pools only (the contraction runs on bf16 matrix cores); zero work is a no-op
     assert lib.pa_prefill(ref(good), 1, 1, 1, 1, 1, 4, 3, 4, 10, 10, 0.1, None) == -2
     bf = pa.pa_pool(0x1000, 16, 4, 16, 64, pa.PA_BF16)
