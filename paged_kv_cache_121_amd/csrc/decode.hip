@@ -260,7 +260,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ int s_poison;
+  __shared__ int s_bad[kWaves];
 
   // One-dimensional grid.  Workgroup wg runs on XCD wg % kXcds; XCD x takes
   // the (sequence, KV head) pairs x, x + kXcds, ..., first partition 0 of
@@ -279,43 +279,60 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int row = lane >> 4, col = lane & 15;
 
+  // ---- loads that do not depend on the context length go out first, so
+  // their latency overlaps that of the length itself: the queries (register
+  // r holds head r ^ sigma(lane), dims col*EPL ...) and, for partition 0 --
+  // which every valid context has -- the partition's block ids.
+  const int64_t head_row0 = ((int64_t)s * num_q_heads + (int64_t)h * G);  // first query/output row
+  const int sigma = (lane % QS) * HPL;
+  Frag<NW> qf[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+    load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
+  static_assert(kMaxPartitionBlocks <= 2 * kThreads, "two table entries per thread");
+  const int blk_begin = p * part_blocks;
+  const int32_t *trow = tables + (int64_t)s * max_blocks_per_seq + blk_begin;
+  int tb[2] = {0, 0};
+  if (p == 0) {
+    const int n = min(part_blocks, max_blocks_per_seq);
+    if (tid < n) tb[0] = trow[tid];
+    if (tid + kThreads < n) tb[1] = trow[tid + kThreads];
+  }
+
   const int L = context_lens[s];
   const int part_tokens = part_blocks * B;
   const int np = partitions_of(L, max_context_len, max_blocks_per_seq * B, part_tokens);
   const int nparts = np < 1 ? 1 : np;
   if (p >= nparts) return;
 
-  const int64_t head_row0 = ((int64_t)s * num_q_heads + (int64_t)h * G);  // first query/output row
   if (np < 0) {
     for (int i = tid; i < G * D; i += kThreads) out[head_row0 * D + i] = __builtin_nanf("");
     return;
   }
 
-  // ---- stage this partition's block ids in LDS (validated)
+  // ---- stage this partition's block ids in LDS (validated; an invalid id
+  // reads block 0 and poisons the workgroup's output)
   const int seq_blocks = (L + B - 1) / B;
-  const int blk_begin = p * part_blocks;
   const int nblk = min(part_blocks, seq_blocks - blk_begin);
-  if (tid == 0) s_poison = 0;
-  __syncthreads();
   // The last unit of a sequence of small blocks may reach past its blocks:
   // those entries read block 0 (in bounds) and all their tokens are masked.
   // Partitions hold whole units, so nunits * R <= part_blocks.
   const int nunits = (nblk + R - 1) / R;
-  for (int i = tid; i < nunits * R; i += kThreads) {
-    int b = i < nblk ? tables[(int64_t)s * max_blocks_per_seq + blk_begin + i] : 0;
-    if (b < 0 || (int64_t)b >= num_blocks) {
-      s_poison = 1;
-      b = 0;
-    }
-    s_tbl[i] = b;
-  }
-
-  // ---- query registers: register r holds head r ^ sigma(lane), dims col*EPL ...
-  const int sigma = (lane % QS) * HPL;
-  Frag<NW> qf[G];
+  bool bad = false;
 #pragma unroll
-  for (int r = 0; r < G; ++r)
-    load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nunits * R) {
+      int b = i >= nblk ? 0 : p == 0 ? tb[k] : trow[i];
+      if (b < 0 || (int64_t)b >= num_blocks) {
+        bad = true;
+        b = 0;
+      }
+      s_tbl[i] = b;
+    }
+  }
+  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;  // all lanes take part
+  if (lane == 0) s_bad[wave] = wave_bad;
   __syncthreads();
 
   float m[HPL], lsum[HPL], o[G][EPL];
@@ -515,7 +532,9 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     }
   }
   __syncthreads();
-  const bool poisoned = s_poison != 0;
+  bool poisoned = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) poisoned |= s_bad[w] != 0;
   for (int i = tid; i < G * D; i += kThreads) {
     const int hh = i / D, d = i - hh * D;
     float M = kNegInf;

@@ -294,3 +294,29 @@ def test_decode_other_supported_shapes(group, head_dim, block_size, dtype):
         err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
         say(f"    partition {part}: max abs err {err:.3e}")
         assert err <= ATOL
+
+
+@pytest.mark.parametrize("hkv,group,partition_size", [(3, 2, 64), (3, 2, 128), (1, 4, 256), (8, 1, 512),
+                                                      (5, 8, 96)])
+def test_decode_mixed_lengths_any_partition_count(hkv, group, partition_size):
+    # many sequences of very different lengths, so most (sequence, head) pairs have fewer
+    # partitions than the call; pair counts that are not multiples of 8; empty and invalid rows
+    rng = np.random.default_rng(hkv * 100 + partition_size)
+    lens = np.clip(np.rint(rng.lognormal(np.log(60), 1.2, size=37)), 1, 700).astype(np.int64)
+    lens[3], lens[20] = 700, 1
+    nb = int(sum(-(-L // 16) for L in lens)) + 4
+    w = make_custom(name="mixed-lengths", seed=61 + hkv, dtype="bf16", num_blocks=nb, num_q_heads=hkv * group,
+                    num_kv_heads=hkv, head_dim=64, block_size=16, lengths=lens)
+    st = w.steps[0]
+    say(f"[mixed] Hkv={hkv} G={group} partition {partition_size}: {len(lens)} sequences, max {lens.max()}")
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, partition_size)
+    assert np.isfinite(got).all() and np.abs(got - want).max() <= ATOL
+    # the same batch with an empty row and a row whose length exceeds the bound
+    bad = st.context_lens.copy()
+    bad[5], bad[11] = 0, 10 ** 6
+    got = _decode_custom(w, w.pool, w.block_tables, bad, st.q, partition_size,
+                         max_context_len=int(w.block_tables.shape[1]) * 16)
+    assert (got[5] == 0).all() and np.isnan(got[11]).all()
+    keep = [s for s in range(len(lens)) if s not in (5, 11)]
+    assert np.abs(got[keep] - want[keep]).max() <= ATOL
