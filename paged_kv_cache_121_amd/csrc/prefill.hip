@@ -69,9 +69,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // permlane32_swap those of (l & ~32, l | 32) -- VALU only, no LDS round trip.
 __device__ __forceinline__ float group_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_min(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -117,8 +117,15 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
                int num_row_tiles, int num_seqs) {
   using C = PfCfg<D>;
   constexpr int QT = kRows / G;  // tokens per workgroup
-  __shared__ __attribute__((aligned(16))) char s_k[2][C::TILEB];
-  __shared__ __attribute__((aligned(16))) char s_v[2][C::TILEB];
+  // Separate LDS objects per buffer: the compiler can then see that a
+  // direct-to-LDS load into one buffer does not touch the other, and does not
+  // make the next tile's reads wait for it.
+  __shared__ __attribute__((aligned(16))) char s_k0[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char s_k1[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char s_v0[C::TILEB];
+  __shared__ __attribute__((aligned(16))) char s_v1[C::TILEB];
+  char *const s_k[2] = {s_k0, s_k1};
+  char *const s_v[2] = {s_v0, s_v1};
   __shared__ __attribute__((aligned(16))) char s_vst[C::TILEB];  // V as loaded (bf16), before conversion
 
   // Work order: (sequence, KV head) pairs one after another, each pair's row
@@ -209,6 +216,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   const char *head_base = pool + (int64_t)h * B * C::ROWB;
   const int64_t kv_half = (int64_t)num_kv_heads * B * C::ROWB;  // K tile to V tile of one block
   const int32_t *table_row = tables + (int64_t)s * max_blocks_per_seq;
+  const int num_blocks32 = (int)num_blocks;  // at most INT32_MAX (checked by the host)
   bool poisoned = false;
 
   // K and V go straight from global memory into LDS (global_load_lds_dwordx4:
@@ -217,49 +225,93 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // of row RPI*(4i+w) + l / NCH16.  For K it loads the chunk the XOR swizzle
   // puts in that slot; V lands unswizzled in a staging tile and is converted
   // to fp16 into its swizzled tile by the same lane (convert_v).  Keys past the
-  // context load the last real key instead (finite; their scores are masked
-  // and their probabilities are exactly 0), so no zero fill is needed.
+  // context are loaded from wherever their rows fall (the last block's tail,
+  // or block 0 past the table's used entries): their scores are masked before
+  // any use and convert_v writes their values as zeros, so whatever those rows
+  // hold never reaches the output.
   constexpr int RPI = 1024 / C::ROWB;  // key rows per instruction
   const int dl_row = lane / C::NCH16, dl_slot = lane % C::NCH16;
-  auto load_lds = [&](int t, int64_t part_off, bool swizzle, char *buf) __attribute__((always_inline)) {
-    int blk[NBT];
+  // this lane's byte offset inside an instruction's RPI rows (K: swizzled chunk)
+  uint32_t lane_off_k[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int row = RPI * (kPfWaves * i + wave) + dl_row;
+    lane_off_k[i] = dl_row * C::ROWB + ((dl_slot ^ (row % C::NCH16)) << 4);
+  }
+  const uint32_t lane_off_v = dl_row * C::ROWB + (dl_slot << 4);
+  // block ids of tile t (scalar loads; fetched a tile ahead of their use)
+  auto fetch_ids = [&](int t, int (&ids)[NBT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
       const int jb = B <= kKeys ? t * NBT + i : t / (B / kKeys);
-      int b = jb < seq_blocks ? table_row[jb] : 0;
-      b = __builtin_amdgcn_readfirstlane(b);
-      if (b < 0 || (int64_t)b >= num_blocks) {
+      ids[i] = __builtin_amdgcn_readfirstlane(jb < seq_blocks ? table_row[jb] : 0);
+    }
+  };
+  auto load_lds = [&](int t, const int (&ids)[NBT], int64_t part_off, bool swizzle, char *buf)
+                      __attribute__((always_inline)) {
+    int blk[NBT];
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) {
+      int b = ids[i];
+      if (b < 0 || b >= num_blocks32) {
         poisoned = true;
         b = 0;
       }
       blk[i] = b;
     }
-    const int last_row = ctx - 1 - t * kKeys;  // rows past it are past the context
+    if constexpr (RPI <= B) {
+      // Every instruction's RPI rows lie in one block, so its address is a
+      // uniform base (scalar registers) plus this lane's fixed offset.  Rows
+      // past the context read whatever the block holds there: their scores
+      // are masked, and convert_v zeroes their values.
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int row = RPI * (kPfWaves * i + wave) + dl_row;
-      const int chunk = swizzle ? dl_slot ^ (row % C::NCH16) : dl_slot;
-      const int src_row = min(row, last_row);
-      int b, rib;
-      if constexpr (B > kKeys) {
-        b = blk[0];
-        rib = (t % (B / kKeys)) * kKeys + src_row;
-      } else {
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int row0 = RPI * (kPfWaves * i + wave);  // uniform
+        int b, rib0;
+        if constexpr (B > kKeys) {
+          b = blk[0];
+          rib0 = (t % (B / kKeys)) * kKeys + row0;
+        } else {
+          const int slot = row0 / B;
+          b = blk[0];
+#pragma unroll
+          for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
+          rib0 = row0 % B;
+        }
+        const uint64_t base = (uint64_t)(head_base + (int64_t)b * 2 * kv_half + part_off + (int64_t)rib0 * C::ROWB);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+        const char *sbase = reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+        const uint32_t off = swizzle ? lane_off_k[i] : lane_off_v;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(sbase + off),
+                                         (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
+                                         16, 0, 0);
+      }
+    } else {
+      // an instruction spans two blocks (64-dim rows, 4-token blocks): per-lane
+      // addresses; rows past the context read the last real row
+      const int last_row = ctx - 1 - t * kKeys;
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int row = RPI * (kPfWaves * i + wave) + dl_row;
+        const int chunk = swizzle ? dl_slot ^ (row % C::NCH16) : dl_slot;
+        const int src_row = min(row, last_row);
         const int slot = src_row / B;
-        b = blk[0];
+        int b = blk[0];
 #pragma unroll
         for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
-        rib = src_row % B;
+        const char *src = head_base + (int64_t)b * 2 * kv_half + part_off + (src_row % B) * C::ROWB + chunk * 16;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
+                                         16, 0, 0);
       }
-      const char *src = head_base + (int64_t)b * 2 * kv_half + part_off + rib * C::ROWB + chunk * 16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                       (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
-                                       16, 0, 0);
     }
   };
   // V from the staging tile (this lane's own loads) to fp16 in its swizzled tile;
   // exact for |v| < 65504 (bf16 keeps 8 significant bits, fp16 11)
-  auto convert_v = [&](char *buf) __attribute__((always_inline)) {
+  // Rows of tile t past the context become zeros.
+  auto convert_v = [&](char *buf, int t) __attribute__((always_inline)) {
+    const int vrows = ctx - t * kKeys;  // rows of the tile inside the context (uniform)
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int row = RPI * (kPfWaves * i + wave) + dl_row;
@@ -269,6 +321,9 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       for (int w = 0; w < 4; ++w)
         vh[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x[w] << 16),
                                                                         __uint_as_float(x[w] & 0xffff0000u)));
+      if (vrows < kKeys) {  // uniform: the context ends inside this tile
+        if (row >= vrows) vh = u32x4_t{0u, 0u, 0u, 0u};
+      }
       *reinterpret_cast<u32x4_t *>(&buf[v_lds8<D>(row, 2 * dl_slot)]) = vh;
     }
   };
@@ -319,25 +374,36 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // O and the row sums when it moves by more than the threshold (rare).
   auto row_max = [&](int t, f32x4_t (&sacc)[kRG][4]) __attribute__((always_inline)) {
     const int k0 = t * kKeys;
+    float mnew[kRG];
+    bool upd[kRG];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       if (k0 + kKeys - 1 > w_pos_min) {  // some key of the tile lies after some row
+        const int lim = my_pos[rg] - k0 - 4 * grp;  // key k0 + 4*grp + c is visible iff c <= lim
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            if (k0 + 16 * kt + 4 * grp + jj > my_pos[rg]) sacc[rg][kt][jj] = kPfNegInf;
+            if (16 * kt + jj > lim) sacc[rg][kt][jj] = kPfNegInf;
       }
-      float mx = kPfNegInf;
+      // NaN-propagating maximum: no operand quieting, and pairs fuse into v_maximum3
+      float mx = __builtin_elementwise_maximum(sacc[rg][0][0], sacc[rg][0][1]);
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[rg][0][2], sacc[rg][0][3]));
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        mx = fmaxf(mx, fmaxf(fmaxf(sacc[rg][kt][0], sacc[rg][kt][1]), fmaxf(sacc[rg][kt][2], sacc[rg][kt][3])));
+      for (int kt = 1; kt < 4; ++kt) {
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[rg][kt][0], sacc[rg][kt][1]));
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[rg][kt][2], sacc[rg][kt][3]));
+      }
       const float mt = group_max(mx) * cs;  // this tile's row maximum, log2 units (-inf if fully masked)
-      const float mn = fmaxf(m[rg], mt);
-      const bool upd = mn > m[rg] + kPfRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-        const float alpha = upd ? pf_exp2(m[rg] - mn) : 1.0f;
-        if (upd) m[rg] = mn;
+      mnew[rg] = __builtin_elementwise_maximum(m[rg], mt);
+      upd[rg] = mnew[rg] > m[rg] + kPfRescaleThreshold;
+    }
+    // one wave-uniform branch for both row groups (rare)
+    if (__builtin_amdgcn_ballot_w64(upd[0] || (kRG > 1 && upd[kRG - 1])) != 0) {
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        const float alpha = upd[rg] ? pf_exp2(m[rg] - mnew[rg]) : 1.0f;
+        if (upd[rg]) m[rg] = mnew[rg];
         // O rows are 4*grp + jj: fetch those rows' factors
         float ar[4];
 #pragma unroll
@@ -391,35 +457,54 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // K(t+1) has been arriving in tile t-1's K buffer; convert V(t+1) from the
   // staging tile into tile t-1's V buffer; barrier; start K(t+2) into tile t's
   // K buffer and V(t+2) into the staging tile.
-  load_lds(0, 0, true, s_k[0]);
-  load_lds(0, kv_half, false, s_vst);
+  int ids[NBT];
+  fetch_ids(0, ids);
+  load_lds(0, ids, 0, true, s_k[0]);
+  load_lds(0, ids, kv_half, false, s_vst);
   wait_lds_loads();
-  convert_v(s_v[0]);
+  convert_v(s_v[0], 0);
   __syncthreads();
   if (ntiles > 1) {
-    load_lds(1, 0, true, s_k[1]);
-    load_lds(1, kv_half, false, s_vst);
+    fetch_ids(1, ids);
+    load_lds(1, ids, 0, true, s_k[1]);
+    load_lds(1, ids, kv_half, false, s_vst);
   }
   f32x4_t sc[kRG][4];
-  auto step = [&](int t, auto bt) __attribute__((always_inline)) {
+  // one tile step; the arithmetic is skipped (COMPUTE false) for tiles past
+  // every row of this wave, which still take part in the loads and barriers
+  auto step = [&](int t, auto bt, auto compute) __attribute__((always_inline)) {
     constexpr int b = decltype(bt)::value;
-    if (t <= w_last_tile) {
+    if (t + 2 < ntiles) fetch_ids(t + 2, ids);  // their latency hides behind this tile's work
+    if constexpr (decltype(compute)::value) {
       qk(s_k[b], sc);
       row_max(t, sc);
       exp_pv(sc, s_v[b]);
     }
     wait_lds_loads();  // K(t+1) has arrived in s_k[1 - b], V(t+1) in the staging tile
-    if (t + 1 < ntiles) convert_v(s_v[1 - b]);
+    if (t + 1 < ntiles) convert_v(s_v[1 - b], t + 1);
     __syncthreads();
     if (t + 2 < ntiles) {
-      load_lds(t + 2, 0, true, s_k[b]);
-      load_lds(t + 2, kv_half, false, s_vst);
+      load_lds(t + 2, ids, 0, true, s_k[b]);
+      load_lds(t + 2, ids, kv_half, false, s_vst);
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, buf0{});
-    if (t + 1 >= ntiles) break;
-    step(t + 1, buf1{});
+  using yes = std::true_type;
+  using no = std::false_type;
+  const int n_compute = min(ntiles, w_last_tile + 1);  // tiles with work for this wave (uniform)
+  int t = 0;
+  for (; t + 1 < n_compute; t += 2) {
+    step(t, buf0{}, yes{});
+    step(t + 1, buf1{}, yes{});
+  }
+  if (t < n_compute) {
+    step(t, buf0{}, yes{});
+    ++t;
+  }
+  for (; t < ntiles; ++t) {
+    if (t & 1)
+      step(t, buf1{}, no{});
+    else
+      step(t, buf0{}, no{});
   }
   const bool seq_poisoned = poisoned;
 
