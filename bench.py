@@ -22,6 +22,8 @@ METRIC = "decode attention KV-read GB/s (and % HBM peak); sequences·layers/sec"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "decode_qwen3_8b_b64_hbm_traffic.md")
+PREFILL_TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                    "prefill_4x4100_hbm_traffic.md")
 
 
 def parse():
@@ -52,28 +54,53 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(name: str = "decode.hip") -> str:
     import hashlib
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_121_amd", "csrc", "decode.hip")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_121_amd", "csrc", name)
     with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_json(path: str):
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    return json.loads(text[start + 7:text.index("```", start + 7)])
 
 
 def measured_traffic(workload: int, partition_size: int):
     """HBM bytes per decode launch from the committed counter summary, if it was
     taken on the current decode kernel source at this partition size; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        text = f.read()
-    start = text.find("```json")
-    if start < 0:
-        return None
-    t = json.loads(text[start + 7:text.index("```", start + 7)])
-    e = t.get(f"workload{workload}")
+    t = _traffic_json(TRAFFIC_FILE)
+    e = t.get(f"workload{workload}") if t else None
     if not e or e.get("decode_source_sha256_16") != kernel_source_digest() or e.get("partition_size") != partition_size:
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def measured_prefill_traffic(k: int):
+    """HBM bytes per prefill launch from the committed counter summary, if it was
+    taken on the current prefill kernel source; else None."""
+    t = _traffic_json(PREFILL_TRAFFIC_FILE)
+    e = t.get(f"prefill{k}") if t else None
+    if not e or e.get("prefill_source_sha256_16") != kernel_source_digest("prefill.hip"):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def prefill_algorithmic_bytes(w) -> int:
+    """Bytes one prefill launch must move at least: each sequence's visible K/V
+    rows once (a block shared by several sequences counts once per sequence),
+    the queries once, the fp32 output once."""
+    elt = 2
+    kv = int(np.sum(w.context_lens)) * 2 * w.num_kv_heads * w.head_dim * elt
+    q = w.total_tokens * w.num_q_heads * w.head_dim * elt
+    out = w.total_tokens * w.num_q_heads * w.head_dim * 4
+    return kv + q + out
 
 
 def settle(fn, ms: float = 100.0, cap: int = 3000):
@@ -244,8 +271,8 @@ def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, cpu: bool 
     """Time pa_prefill on prefill workload k (chunk K/V written first by pa_cache_write).
 
     Algorithmic work = the causal attention's multiply-adds: 4 * D * Hq flops
-    per (query row, visible key).  The bf16 high/low split of P is counted as
-    overhead, not as work."""
+    per (query row, visible key); the row sums the kernel forms on the matrix
+    cores and the masked halves of diagonal tiles are overhead, not work."""
     import torch
 
     import paged_kv_cache_121_amd as pa
@@ -288,8 +315,10 @@ def prefill_measurement(k: int, dev, reps: int = 20, warmup: int = 3, cpu: bool 
     return {"workload": f"prefill workload {k}: {PREFILL_NAMES[k]}", "tokens": w.total_tokens,
             "flops": flops, "us": round(ms * 1e3, 1), "tflops": round(tflops, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_prefill_traffic(k), "kernel": "prefill_kernel",
+                         "algorithmic_flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": prefill_algorithmic_bytes(w)},
             "cpu_baseline": base,
             "sampled_max_abs_err": base["max_abs_err_vs_gpu"] if base else None}
 
