@@ -53,7 +53,7 @@ def test_prefill_small_workloads_match_oracle(k):
 
 @pytest.mark.parametrize("group,head_dim,block_size", [
     (1, 128, 16), (2, 128, 32), (4, 64, 16), (8, 128, 32), (8, 64, 16), (4, 128, 32),
-    (4, 128, 4), (2, 64, 8), (4, 128, 64), (8, 128, 128), (1, 64, 128),
+    (4, 128, 4), (2, 64, 8), (2, 64, 4), (4, 128, 64), (8, 128, 128), (1, 64, 128),
 ])
 def test_prefill_shapes_chunks_and_ragged_tails(group, head_dim, block_size):
     hkv = 2
