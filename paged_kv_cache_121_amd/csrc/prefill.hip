@@ -63,7 +63,7 @@ __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Max / min over the four 16-lane groups of the wave (lanes l, l^16, l^32,
+// Maximum over the four 16-lane groups of the wave (lanes l, l^16, l^32,
 // l^48) with the gfx950 row-swap permutes: with both operands the same value,
 // permlane16_swap yields the values of lanes (l & ~16, l | 16) and
 // permlane32_swap those of (l & ~32, l | 32) -- VALU only, no LDS round trip.
@@ -72,12 +72,6 @@ __device__ __forceinline__ float group_max(float x) {
   x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_min(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int D>
