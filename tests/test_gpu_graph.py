@@ -1,0 +1,74 @@
+"""A whole decode step captured in a HIP graph and replayed.
+
+Every entry point of the library only enqueues kernels on the caller's stream
+(no allocation, no synchronisation, no memset), so a serving loop can capture
+a step -- copy-on-write block copies, slot mapping, cache write, decode -- once
+and replay it.  The graph is replayed several times, with the program's own
+eager work and synchronisations between replays, and every replay must
+reproduce the eager step bit for bit: the output and the whole pool.
+"""
+
+import pytest
+import torch
+
+import paged_kv_cache_121_amd as pa
+from workloads import make_config
+
+from _gpu_util import DEV, i32, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("k,partition_size", [(3, 0), (3, 64), (5, 0), (1, 32)])
+def test_decode_step_replays_in_a_graph(k, partition_size):
+    w = make_config(k, small=True)
+    st = w.steps[0]
+    say(f"[graph] {w.name} partition_size={partition_size} cow_pairs={len(st.cow_src)}")
+    pool0 = to_dev(w.pool, w.dtype)
+    pool = pa.PagedKVPool(pool0.clone())
+    tables, seqs, pos, lens = i32(w.block_tables), i32(st.write_seq), i32(st.write_pos), i32(st.context_lens)
+    q, kn, vn = to_dev(st.q, w.dtype), to_dev(st.k_new, w.dtype), to_dev(st.v_new, w.dtype)
+    src, dst = i32(st.cow_src), i32(st.cow_dst)
+    S, Hq, D = (int(x) for x in q.shape)
+    mcl = int(st.context_lens.max())
+    slots = torch.empty(len(st.write_pos), dtype=torch.int64, device=DEV)
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device=DEV)
+    need = pa.pa_decode_workspace_size(pool, S, Hq, mcl, partition_size)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    keep = bool(w.meta.get("prefix_tokens"))
+
+    def step():
+        if len(st.cow_src):
+            pa.pa_block_copy(pool, src, dst)
+        pa.pa_slot_mapping(pool, tables, seqs, pos, out=slots)
+        pa.pa_cache_write(pool, kn, vn, slots)
+        pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=mcl,
+                     partition_size=partition_size, out=out, workspace=ws, keep_cached=keep)
+
+    step()
+    torch.cuda.synchronize()
+    want_out, want_pool = out.clone(), bits(pool.data).clone()
+
+    pool.data.copy_(pool0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(pool.data), bits(pool0))  # capture records, it does not run
+
+    for r in range(3):
+        pool.data.copy_(pool0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {r}: output differs from the eager step"
+        assert torch.equal(bits(pool.data), want_pool), f"replay {r}: pool differs from the eager step"
+        # the program's own eager work between replays
+        assert torch.isfinite((q.float() * 2).sum()).item()
+    del g
