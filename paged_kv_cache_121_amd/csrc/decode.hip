@@ -54,6 +54,7 @@ namespace {
 #define PA_DECODE_PREFETCH 1
 #endif
 
+constexpr int kShortPartitionTokens = 2048;  // groups of 8: 8-token stages up to this partition
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup L is dispatched to XCD L % 8
 constexpr int kWaves = 4;
 // Chunks in flight ahead of the one being processed.  Measured on the
@@ -593,10 +594,19 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds) * kXcds * a.num_partitions);
   // Pipeline stage: 4 tokens for groups up to 4 (less in flight per wave,
   // and short contexts reach their first score sooner: up to 27 % faster on
-  // 128-token contexts, the same on long ones); 16 for groups of 8, whose
-  // larger per-token arithmetic wants the longer stages on long contexts.
-  constexpr int CH = G <= 4 ? 4 : 16;
-  auto kernel = a.stream_loads ? decode_kernel<T, D, B, G, CH, true> : decode_kernel<T, D, B, G, CH, false>;
+  // 128-token contexts, the same on long ones).  Groups of 8 carry twice the
+  // arithmetic per token: 8-token stages while partitions are short (many
+  // (sequence, head) pairs, typically a mixed batch), 16-token stages for
+  // the long partitions of few long sequences.
+  auto pick = [&](auto ch) {
+    constexpr int CH = decltype(ch)::value;
+    return a.stream_loads ? decode_kernel<T, D, B, G, CH, true> : decode_kernel<T, D, B, G, CH, false>;
+  };
+  using ch4 = std::integral_constant<int, 4>;
+  using ch8 = std::integral_constant<int, 8>;
+  using ch16 = std::integral_constant<int, 16>;
+  auto kernel = pick(ch4{});
+  if constexpr (G > 4) kernel = a.partition_blocks * B <= kShortPartitionTokens ? pick(ch8{}) : pick(ch16{});
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
