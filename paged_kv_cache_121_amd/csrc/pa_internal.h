@@ -13,9 +13,10 @@ namespace pa {
 // Largest partition, in blocks, whose table entries one workgroup stages in LDS.
 constexpr int kMaxPartitionBlocks = 512;
 // Query rows (GQA head x token) one prefill workgroup takes: 16 per row group,
-// two groups per wave, 4 waves.
+// two groups per wave, 8 waves.
 constexpr int kPrefillRowGroups = 2;
-constexpr int kPrefillRows = 64 * kPrefillRowGroups;
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillRows = 16 * kPrefillRowGroups * kPrefillWaves;
 
 struct PoolDesc {
   char *base;

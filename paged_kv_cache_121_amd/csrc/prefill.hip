@@ -8,10 +8,11 @@
 // over cached positions 0 .. p, found through the block table.
 //
 // Unlike decode this is a dense contraction, so it runs on the matrix cores.
-// One workgroup of 4 waves takes 128 query rows of one KV head (32 per wave,
+// One workgroup of 8 waves takes 256 query rows of one KV head (32 per wave,
 // two 16-row groups sharing every K and V operand read): rows are (head of
 // the GQA group, token) pairs, head-major, so every row of the workgroup
-// reads the same K/V.  K/V tiles of 64 keys go from HBM straight into LDS
+// reads the same K/V, and each K/V tile is loaded and converted once for 8
+// waves (one workgroup per CU at two waves per SIMD).  K/V tiles of 64 keys go from HBM straight into LDS
 // (global_load_lds_dwordx4, no registers on the way), double-buffered, and
 // each wave computes flash-attention style on its rows:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; A = K rows from LDS (ds_read_b128,
@@ -42,7 +43,7 @@ namespace pa {
 namespace {
 
 constexpr int kXcds = 8;  // accelerator complex dies (each with its own L2)
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = kPrefillWaves;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kRG = kPrefillRowGroups;  // 16-row groups per wave
 constexpr int kRows = kPrefillRows;      // query rows per workgroup
@@ -100,8 +101,9 @@ __device__ __forceinline__ int v_lds8(int key, int c8) {
   return key * PfCfg<D>::ROWB + ((c8 ^ (4 * (key % (PfCfg<D>::NCH8 / 4)))) << 3);
 }
 
-// Two waves per SIMD: the register budget that lets two workgroups share a
-// compute unit (their LDS fits as well), so one's loads overlap the other's math.
+// Two waves per SIMD (at most 256 registers each): a workgroup's 8 waves fill
+// the four SIMDs of a compute unit twice, so while one wave of a SIMD waits on
+// LDS, memory or the barrier, the other can issue.
 template <int D, int B, int G>
 __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads, const char *__restrict__ q,
