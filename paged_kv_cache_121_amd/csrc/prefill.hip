@@ -49,6 +49,7 @@ constexpr int kRG = kPrefillRowGroups;  // 16-row groups per wave
 constexpr int kRows = kPrefillRows;      // query rows per workgroup
 static_assert(kRows == 16 * kRG * kPfWaves, "16 * kRG rows per wave");
 constexpr int kKeys = 64;             // keys per LDS tile
+constexpr int kVAhead = 4;            // P.V operand reads in flight ahead of their MFMAs
 constexpr float kPfNegInf = -__builtin_inff();
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfRescaleThreshold = 8.0f;
@@ -431,19 +432,32 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       for (int ks = 0; ks < 2; ++ks)
         osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
     }
+    // V operands are read kVAhead steps before the MFMAs that use them, and
+    // the schedule is pinned to (2 reads of a later step, 2 MFMAs of this one)
+    // so the reads' latency overlaps the matrix work (left to itself the
+    // scheduler waits on each step's reads just before its MFMAs; 2 % slower).
+    constexpr int NS = 2 * C::NT;  // (nt, ks) steps
+    f16x8_t vq[kVAhead];
+    auto rdv = [&](int st) __attribute__((always_inline)) {
+      const int nt = st / 2, ks = st % 2;
+      const i16x4_t lo4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
+      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
+      return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
+    for (int st = 0; st < kVAhead; ++st) vq[st] = rdv(st);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const i16x4_t lo4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
-        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
-        const f16x8_t vb = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int st = 0; st < NS; ++st) {
+      const int nt = st / 2, ks = st % 2;
+      const f16x8_t vb = vq[st % kVAhead];
+      if (st + kVAhead < NS) vq[st % kVAhead] = rdv(st + kVAhead);
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
-      }
+      for (int rg = 0; rg < kRG; ++rg)
+        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
     }
   };
 
