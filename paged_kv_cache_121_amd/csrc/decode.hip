@@ -54,14 +54,16 @@ namespace {
 #define PA_DECODE_PREFETCH 1
 #endif
 
-constexpr int kShortPartitionTokens = 2048;  // groups of 8: 8-token stages up to this partition
+// Partitions of kMidPartitionMin..kShortPartitionTokens tokens (mixed batches
+// of many pairs) take 8-wave workgroups and 8-token stages; groups of 8 take
+// 8-token stages up to kShortPartitionTokens.
+constexpr int kShortPartitionTokens = 2048;
+constexpr int kMidPartitionMin = 1024;
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup L is dispatched to XCD L % 8
-constexpr int kWaves = 4;
 // Chunks in flight ahead of the one being processed.  Measured on the
 // Qwen3-8B batch-64 layer: 1 ahead already hides the latency (2 ahead was
 // 3 % slower, it costs 20 more VGPRs).
 constexpr int kPrefetch = PA_DECODE_PREFETCH;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -245,14 +247,16 @@ struct Cfg {
 // the Qwen3-8B batch-64 layer it raised decode bandwidth from 5.8 to 6.4
 // TB/s.  Batches whose sequences share blocks want the normal policy instead
 // (the later readers of a shared block hit in L2).
-template <typename T, int D, int B, int G, int CH, bool NT>
-__global__ void __launch_bounds__(kThreads)
+template <typename T, int D, int B, int G, int CH, int W, bool NT>
+__global__ void __launch_bounds__(64 * W)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
               int max_blocks_per_seq, const int32_t *__restrict__ context_lens, int num_q_heads,
               float scale_log2, int max_context_len, int part_blocks, int max_parts, int num_pairs,
               float *__restrict__ ws_o, float *__restrict__ ws_ml) {
   using C = Cfg<T, D, B, G, CH>;
+  constexpr int kWaves = W;  // wavefronts per workgroup
+  constexpr int kThreads = 64 * W;
   constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB, R = C::R;
   constexpr int NS = C::STEPS;
   static_assert(B % 4 == 0 && (B < CH ? CH % B == 0 : B % CH == 0), "block size");
@@ -592,22 +596,36 @@ template <typename T, int D, int B, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   const int pairs = a.num_seqs * a.pool.num_kv_heads;
   const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds) * kXcds * a.num_partitions);
-  // Pipeline stage: 4 tokens for groups up to 4 (less in flight per wave,
-  // and short contexts reach their first score sooner: up to 27 % faster on
-  // 128-token contexts, the same on long ones).  Groups of 8 carry twice the
-  // arithmetic per token: 8-token stages while partitions are short (many
-  // (sequence, head) pairs, typically a mixed batch), 16-token stages for
-  // the long partitions of few long sequences.
-  auto pick = [&](auto ch) {
-    constexpr int CH = decltype(ch)::value;
-    return a.stream_loads ? decode_kernel<T, D, B, G, CH, true> : decode_kernel<T, D, B, G, CH, false>;
+  // Work shape per launch (measured on MI355X; see the partition choice):
+  // - groups up to 4: 4-waves workgroups with 4-token stages (less in flight
+  //   per wave; short contexts reach their first score sooner: up to 27 %
+  //   faster on 128-token contexts, the same on long ones), except partitions
+  //   of 1,024-2,048 tokens -- the many-pair mixed batches -- which take 8 waves
+  //   and 8-token stages (4-6 % faster there; 4 % slower on 4,096-token
+  //   partitions, 39 % slower on 256-token ones);
+  // - groups of 8 carry twice the arithmetic per token: 8-token stages up to
+  //   2,048-token partitions, 16-token stages for the long partitions of a few
+  //   long sequences.
+  auto pick = [&](auto ch, auto w) {
+    constexpr int CH = decltype(ch)::value, W = decltype(w)::value;
+    return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true> : decode_kernel<T, D, B, G, CH, W, false>;
   };
   using ch4 = std::integral_constant<int, 4>;
   using ch8 = std::integral_constant<int, 8>;
   using ch16 = std::integral_constant<int, 16>;
-  auto kernel = pick(ch4{});
-  if constexpr (G > 4) kernel = a.partition_blocks * B <= kShortPartitionTokens ? pick(ch8{}) : pick(ch16{});
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
+  using w4 = std::integral_constant<int, 4>;
+  using w8 = std::integral_constant<int, 8>;
+  const int part_tokens = a.partition_blocks * B;
+  const bool mid = part_tokens >= kMidPartitionMin && part_tokens <= kShortPartitionTokens;
+  auto kernel = pick(ch4{}, w4{});
+  int waves = 4;
+  if constexpr (G > 4) {
+    kernel = part_tokens <= kShortPartitionTokens ? pick(ch8{}, w4{}) : pick(ch16{}, w4{});
+  } else if (mid) {
+    kernel = pick(ch8{}, w8{});
+    waves = 8;
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,
