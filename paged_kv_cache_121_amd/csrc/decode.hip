@@ -8,7 +8,7 @@
 // Work decomposition
 //   one workgroup per (partition p, KV head h, sequence s), in a
 //   one-dimensional grid ordered so each XCD gets an equal share of the
-//   (sequence, head) pairs.  A workgroup of kWaves
+//   (sequence, head) pairs.  A workgroup of kWaves (4 or 8, chosen per launch)
 //   wavefronts serves all G = Hq / Hkv query heads of KV head h, so each K/V
 //   byte is read from HBM once per step.  The workgroup owns the blocks
 //   [p * part, (p + 1) * part) of the sequence; wave w takes the workgroup's
@@ -77,9 +77,13 @@ constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 constexpr int quad_bcast(int k) { return k * 0x55; }  // [k,k,k,k]
 
+// Every control used here (quad permutes, row rotates) reads a valid lane of
+// the same 16-lane row for every lane, and all rows and banks are written, so
+// the "old" operand is never used: bound_ctrl lets the compiler drop it and
+// fold the permute into the instruction that consumes it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
