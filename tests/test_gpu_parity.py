@@ -320,3 +320,23 @@ def test_decode_mixed_lengths_any_partition_count(hkv, group, partition_size):
     assert (got[5] == 0).all() and np.isnan(got[11]).all()
     keep = [s for s in range(len(lens)) if s not in (5, 11)]
     assert np.abs(got[keep] - want[keep]).max() <= ATOL
+
+
+@pytest.mark.parametrize("group,dtype,partition_size", [(4, "bf16", 1024), (2, "f32", 2048), (4, "f32", 1536),
+                                                        (8, "bf16", 2048), (8, "f32", 4096), (1, "bf16", 4096)])
+def test_decode_work_shapes_by_partition(group, dtype, partition_size):
+    # the launch picks its work shape from the group size and the partition length:
+    # 4 waves with 4-token stages, 8 waves with 8-token stages (1,024-2,048-token
+    # partitions), or for groups of 8 the 8- or 16-token stages; every shape against the oracle
+    hkv = 2
+    rng = np.random.default_rng(group * 7 + partition_size)
+    lens = np.clip(np.rint(rng.lognormal(np.log(900), 1.0, size=19)), 1, 6000).astype(np.int64)
+    lens[0], lens[1] = 6000, 2 * partition_size + 1
+    nb = int(sum(-(-L // 16) for L in lens)) + 4
+    w = make_custom(name="work-shapes", seed=71 + group, dtype=dtype, num_blocks=nb, num_q_heads=hkv * group,
+                    num_kv_heads=hkv, head_dim=128, block_size=16, lengths=lens)
+    st = w.steps[0]
+    say(f"[work shapes] G={group} {dtype} partition {partition_size}: max {lens.max()}")
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, partition_size)
+    assert np.isfinite(got).all() and np.abs(got - want).max() <= ATOL
