@@ -448,6 +448,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     };
 #pragma unroll
     for (int st = 0; st < kVAhead; ++st) vq[st] = rdv(st);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const int nt = st / 2, ks = st % 2;
@@ -459,6 +460,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   using buf0 = std::integral_constant<int, 0>;
@@ -486,7 +488,12 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     constexpr int b = decltype(bt)::value;
     if (t + 2 < ntiles) fetch_ids(t + 2, ids);  // their latency hides behind this tile's work
     if constexpr (decltype(compute)::value) {
+      // The MFMA phases run at raised wave priority, so the arbiter keeps
+      // feeding the matrix pipe while the other wave of the SIMD is in its
+      // softmax (1-2 % measured).
+      __builtin_amdgcn_s_setprio(1);
       qk(s_k[b], sc);
+      __builtin_amdgcn_s_setprio(0);
       row_max(t, sc);
       exp_pv(sc, s_v[b]);
     }
