@@ -55,10 +55,17 @@ def parse():
 
 
 def kernel_source_digest(name: str = "decode.hip") -> str:
+    """Digest of a kernel source's code: comments and blank lines are left out,
+    so a comment edit does not invalidate counters taken on the same code."""
     import hashlib
+    import re
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_121_amd", "csrc", name)
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(src) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _traffic_json(path: str):

@@ -1,6 +1,7 @@
 """Oracle bookkeeping: block counts, slot usage, waste and KV byte sizes.
 
-TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Integers only.
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``, which also lists the page
+titles behind the citation keys).  Integers only.
 """
 
 from __future__ import annotations

@@ -1,6 +1,7 @@
 """Oracle block pool: free list, reference counts, growth and copy-on-write.
 
-TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Pure Python.  This is
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``, which also lists the page
+titles behind the citation keys).  Pure Python.  This is
 the bookkeeping the pages describe around the kernels; it pins the pages'
 worked examples and checks the structure of generated workloads.  It moves no
 data: a copy-on-write returns the (source, destination) pair that a block copy

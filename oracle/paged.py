@@ -1,6 +1,7 @@
 """Oracle for the paged KV-cache hot path: translation, writes, copies, decode.
 
-TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain numpy; floating
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``, which also lists the page
+titles behind the citation keys).  Plain numpy; floating
 point in float64.  The product HIP path never imports this module.
 
 Storage conventions (inputs arrive exactly as the GPU stores them):

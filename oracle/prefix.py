@@ -1,6 +1,7 @@
 """Oracle prefix cache: chained block hashes over the block pool.
 
-TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Pure Python, slow and
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``, which also lists the page
+titles behind the citation keys).  Pure Python, slow and
 direct.  It follows [TSS] "Sharing a prefix: one copy for many requests": each
 full block is named by a hash of its own tokens and of the previous block's
 hash, so the hash of block j stands for the whole prompt up to the end of

@@ -1,6 +1,7 @@
 """Oracle swap-out / swap-in of sequences between the GPU block pool and a host pool.
 
-TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Pure Python.  It
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``, which also lists the page
+titles behind the citation keys).  Pure Python.  It
 follows [VIBE] "The vLLM procedure" steps 7 and 8 (when blocks run out, all
 of a sequence's blocks are evicted at once, sequences sharing blocks are
 evicted together, and evicted blocks are copied to CPU memory and copied back

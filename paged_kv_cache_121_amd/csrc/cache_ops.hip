@@ -1,4 +1,6 @@
 // Slot mapping, cache write and block copy kernels for gfx950.
+// Citation keys ([HRL], [VIBE], [TSS], ...) name the source pages listed with
+// their titles at the top of include/pa.h.
 //
 // All three are pure data movement.  The cache write and the block copy move
 // 16-byte words per lane so that a wavefront touches whole, contiguous

@@ -1,4 +1,6 @@
 // Paged decode attention for gfx950 (CDNA4, wave64).
+// Citation keys ([HRL], [VIBE], [TSS], ...) name the source pages listed with
+// their titles at the top of include/pa.h.
 //
 // What is computed ([HRL] section 8; [VIBE] vLLM procedure step 5): for every
 // sequence s and query head hq, out = softmax(scale * q K^T) V over the

@@ -1,4 +1,6 @@
 // Prefill / chunked-prefill attention over the paged cache for gfx950.
+// Citation keys ([HRL], [VIBE], [TSS], ...) name the source pages listed with
+// their titles at the top of include/pa.h.
 //
 // What is computed ([HRL] section 9, prefill runs a prompt's tokens together;
 // [TSS] "Next", chunked prefill takes a prompt a piece at a time; [HRL]

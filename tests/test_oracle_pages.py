@@ -1,6 +1,8 @@
 """Pins of the oracle's bookkeeping and address translation to numbers the pages print.
 
 Each fixture under tests/golden/ names the page and section it comes from.
+
+Citation keys ([HRL], [TSS], [VIBE], ...): the page titles listed in oracle/__init__.py.
 """
 
 import json

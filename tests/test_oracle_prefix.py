@@ -4,6 +4,8 @@
 only full blocks shared, a hit capped at the prompt minus one token, cached
 blocks kept after free; "Measured: the same prompt, sixteen at a time": the
 peak block counts and the computed-token count of the prefix-repetition run.
+
+Citation keys ([HRL], [TSS], [VIBE], ...): the page titles listed in oracle/__init__.py.
 """
 
 import hashlib

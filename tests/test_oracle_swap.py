@@ -5,6 +5,8 @@ once, sequences sharing blocks leave together, and evicted blocks come back
 from CPU memory later; [HRL] §12: blocks of lower-priority requests move to
 CPU memory.  The data tests move real block contents with the pairs a swap
 returns and check that every sequence reads back exactly what it held.
+
+Citation keys ([HRL], [TSS], [VIBE], ...): the page titles listed in oracle/__init__.py.
 """
 
 import numpy as np
