@@ -147,6 +147,8 @@ __device__ __forceinline__ void widen(const Frag<NW> &f, float (&x)[EPL]) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Partial dot of one lane's EPL dims: query (held as stored words) . key.
 template <typename T, int NW>
@@ -217,6 +219,28 @@ __device__ __forceinline__ float head_value(const float (&v)[HPL], int hh) {
   }
 }
 
+// Matrix-core layout (groups of 8, bf16): the value lane hh of each 16-lane
+// row holds, in every lane of that row (DPP row_newbcast).
+__device__ __forceinline__ float row_lane_value(float v, int hh) {
+  switch (hh) {
+    case 0: return dpp<0x150>(v);
+    case 1: return dpp<0x151>(v);
+    case 2: return dpp<0x152>(v);
+    case 3: return dpp<0x153>(v);
+    case 4: return dpp<0x154>(v);
+    case 5: return dpp<0x155>(v);
+    case 6: return dpp<0x156>(v);
+    default: return dpp<0x157>(v);
+  }
+}
+
+// Per-head value hh in every lane, for either lane layout.
+template <int G, int HPL, bool MQ>
+__device__ __forceinline__ float head_bcast(const float (&v)[HPL], int hh) {
+  if constexpr (MQ) return row_lane_value(v[0], hh);
+  else return head_value<G, HPL>(v, hh);
+}
+
 // Partitions a sequence of length L spans (0 when its outputs are set by
 // the first partition alone: empty or invalid context).  Both kernels use
 // this one definition.
@@ -253,7 +277,18 @@ struct Cfg {
 // the Qwen3-8B batch-64 layer it raised decode bandwidth from 5.8 to 6.4
 // TB/s.  Batches whose sequences share blocks want the normal policy instead
 // (the later readers of a shared block hit in L2).
-template <typename T, int D, int B, int G, int CH, int W, bool NT>
+//
+// MQ: the scores come from the matrix cores (bf16, groups of 8, blocks of 16
+// tokens or more; 16-token stages).  Per stage, S^T = K Q^T is one
+// v_mfma_f32_16x16x32_bf16 per 32 dims: A = K with lane (g, c) = (lane / 16,
+// lane % 16) holding token c, dims 32k + 8g ...; B = Q^T with that lane
+// holding head c (zero for c >= G) at the same dims.  The result leaves lane
+// (g, c) the scores of tokens 4g .. 4g + 3 for head c, so lane (g, c) runs the
+// online softmax of head c over stream g (tokens 4g .. 4g + 3 of every
+// stage).  V keeps the vector layout with the token order matched: at load
+// step i row r holds token 4r + i, and takes head hh's probability and
+// rescale factor from lane hh of its row.
+template <typename T, int D, int B, int G, int CH, int W, bool NT, bool MQ>
 __global__ void __launch_bounds__(64 * W)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
@@ -263,9 +298,14 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   using C = Cfg<T, D, B, G, CH>;
   constexpr int kWaves = W;  // wavefronts per workgroup
   constexpr int kThreads = 64 * W;
-  constexpr int EPL = C::EPL, NW = C::NW, HPL = C::HPL, QS = C::QS, CPB = C::CPB, R = C::R;
+  constexpr int EPL = C::EPL, NW = C::NW, CPB = C::CPB, R = C::R;
   constexpr int NS = C::STEPS;
+  constexpr int HPL = MQ ? 1 : C::HPL, QS = MQ ? G : C::QS;
+  constexpr int KC = D / 32;           // MQ: matrix-core steps per stage (32 dims each)
+  constexpr int KW = MQ ? 4 : NW;      // K words per lane per load
+  constexpr int KN = MQ ? KC : NS;     // K loads per stage
   static_assert(B % 4 == 0 && (B < CH ? CH % B == 0 : B % CH == 0), "block size");
+  static_assert(!MQ || (!std::is_same_v<T, float> && G == 8 && CH == 16 && B >= CH), "matrix-core layout");
 
   __shared__ int s_tbl[kMaxPartitionBlocks];
   __shared__ float s_o[kWaves][G][D];
@@ -295,11 +335,19 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // r holds head r ^ sigma(lane), dims col*EPL ...) and, for partition 0 --
   // which every valid context has -- the partition's block ids.
   const int64_t head_row0 = ((int64_t)s * num_q_heads + (int64_t)h * G);  // first query/output row
-  const int sigma = (lane % QS) * HPL;
-  Frag<NW> qf[G];
+  Frag<KW> qf[MQ ? KC : G];
+  if constexpr (MQ) {
 #pragma unroll
-  for (int r = 0; r < G; ++r)
-    load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
+    for (int kc = 0; kc < KC; ++kc) {
+      qf[kc] = Frag<KW>{};
+      if (col < G) load_frag<KW>(qf[kc], q + ((head_row0 + col) * D + 32 * kc + 8 * row) * C::kElem);
+    }
+  } else {
+    const int sigma = (lane % QS) * HPL;
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+      load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
+  }
   static_assert(kMaxPartitionBlocks <= 2 * kThreads, "two table entries per thread");
   const int blk_begin = p * part_blocks;
   const int32_t *trow = tables + (int64_t)s * max_blocks_per_seq + blk_begin;
@@ -363,9 +411,20 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   const int64_t v_off = (int64_t)num_kv_heads * C::TILE;
   const int lane_off = lane * C::VEC;
 
-  auto issue = [&](int ci, Frag<NW> (&kf)[NS], Frag<NW> (&vf)[NS]) {
+  auto issue = [&](int ci, Frag<KW> (&kf)[KN], Frag<NW> (&vf)[NS]) {
     const int unit = wave + (ci / CPB) * kWaves;
-    if constexpr (R == 1) {
+    if constexpr (MQ) {
+      // K: token col, bytes 64 kc + 16 row of its row; V: token 4 row + i, dims col * EPL ...
+      const int sub = ci % CPB;
+      const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
+      const char *cp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK;
+      const char *kp = cp + col * C::ROW + 16 * row;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) load_frag<KW, NT>(kf[kc], kp + 64 * kc);
+      const char *vp = cp + v_off + 4 * row * C::ROW + col * C::VEC;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) load_frag<NW, NT>(vf[i], vp + i * C::ROW);
+    } else if constexpr (R == 1) {
       const int sub = ci % CPB;
       const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
       const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
@@ -387,7 +446,58 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
       for (int j = 0; j < NS; ++j) load_frag<NW, NT>(vf[j], kp[j] + v_off);
     }
   };
-  auto process = [&](int ci, const Frag<NW> (&kf)[NS], const Frag<NW> (&vf)[NS]) {
+  // (each layout's body is instantiated only for its own kernels)
+  auto process_mq = [&](int ci, const auto &kf, const auto &vf) {
+    if constexpr (MQ) {
+      const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
+      const bool partial = tok0 + CH > L;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kc].w),
+                                                      __builtin_bit_cast(bf16x8_t, qf[kc].w), acc, 0, 0, 0);
+      // lane (row, col): scores of tokens tok0 + 4 row + i for head col
+      float sc[4];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = (!partial || tok0 + 4 * row + i < L) ? acc[i] * scale_log2 : kNegInf;
+      const float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float mn = fmaxf(m[0], cm);
+      const bool upd = mn > m[0] + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        const float alpha[1] = {upd ? fast_exp2(m[0] - mn) : 1.0f};
+        lsum[0] *= alpha[0];
+        m[0] = upd ? mn : m[0];
+  #pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float a = head_bcast<G, HPL, MQ>(alpha, hh);
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) o[hh][e] *= a;
+        }
+      }
+      const float ms = m[0] == kNegInf ? 0.0f : m[0];
+      float pr[4][1];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i][0] = fast_exp2(sc[i] - ms);
+      lsum[0] += (pr[0][0] + pr[1][0]) + (pr[2][0] + pr[3][0]);
+      // PV: load step i holds token 4 row + i in row `row`
+  #pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        float v[EPL];
+        widen<T, NW, EPL>(vf[i], v);
+        if (partial && !(tok0 + 4 * row + i < L)) {
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) v[e] = 0.0f;
+        }
+  #pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pb = head_bcast<G, HPL, MQ>(pr[i], hh);
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pb, v[e], o[hh][e]);
+        }
+      }
+    }
+  };
+  auto process_vec = [&](int ci, const auto &kf, const auto &vf) {
     const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
     const bool partial = tok0 + CH > L;
     // QK for the 4 tokens this row sees in the chunk
@@ -459,6 +569,10 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
       }
     }
   };
+  auto process = [&](int ci, const Frag<KW> (&kf)[KN], const Frag<NW> (&vf)[NS]) {
+    if constexpr (MQ) process_mq(ci, kf, vf);
+    else process_vec(ci, kf, vf);
+  };
 
   // ---- main loop: double-buffered K/V chunks, two per iteration with no
   // exit in between.  Every load is issued unconditionally (the prefetch past
@@ -467,7 +581,10 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // process() waits for its own chunk while the next one is in flight.
   if constexpr (kPrefetch == 1) {
     if (nch > 0) {
-      Frag<NW> kA[NS], vA[NS], kB[NS], vB[NS];
+      Frag<KW> kA[KN];
+      Frag<NW> vA[NS];
+      Frag<KW> kB[KN];
+      Frag<NW> vB[NS];
       const int last = nch - 1;
       issue(0, kA, vA);
       int ci = 0;
@@ -483,7 +600,12 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     static_assert(kPrefetch == 2, "prefetch depth 1 or 2");
     // three buffers, two chunks in flight while one is processed
     if (nch > 0) {
-      Frag<NW> kA[NS], vA[NS], kB[NS], vB[NS], kC[NS], vC[NS];
+      Frag<KW> kA[KN];
+      Frag<NW> vA[NS];
+      Frag<KW> kB[KN];
+      Frag<NW> vB[NS];
+      Frag<KW> kC[KN];
+      Frag<NW> vC[NS];
       const int last = nch - 1;
       issue(0, kA, vA);
       issue(min(1, last), kB, vB);
@@ -518,8 +640,8 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float b1 = head_value<G, HPL>(a1, hh);
-      const float b2 = head_value<G, HPL>(a2, hh);
+      const float b1 = head_bcast<G, HPL, MQ>(a1, hh);
+      const float b2 = head_bcast<G, HPL, MQ>(a2, hh);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const float o2 = __shfl_xor(o[hh][e], off);
@@ -598,6 +720,11 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
   out[row * D + d] = num / den;
 }
 
+// The one rule for which launches take their scores from the matrix cores.
+constexpr bool matrix_core_scores(bool bf16, int group, int block_size) {
+  return bf16 && group == 8 && block_size >= 16;
+}
+
 template <typename T, int D, int B, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   const int pairs = a.num_seqs * a.pool.num_kv_heads;
@@ -609,13 +736,17 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   //   of 1,024-2,048 tokens -- the many-pair mixed batches -- which take 8 waves
   //   and 8-token stages (4-6 % faster there; 4 % slower on 4,096-token
   //   partitions, 39 % slower on 256-token ones);
-  // - groups of 8 carry twice the arithmetic per token: 8-token stages up to
-  //   2,048-token partitions, 16-token stages for the long partitions of a few
-  //   long sequences.
-  auto pick = [&](auto ch, auto w) {
+  // - groups of 8 carry twice the arithmetic per token: bf16 pools with
+  //   blocks of 16 or more take their scores from the matrix cores
+  //   (16-token stages); otherwise 8-token stages up to 2,048-token
+  //   partitions, 16-token stages for the long partitions of a few long
+  //   sequences.
+  auto pick = [&](auto ch, auto w, auto mq) {
     constexpr int CH = decltype(ch)::value, W = decltype(w)::value;
-    return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true> : decode_kernel<T, D, B, G, CH, W, false>;
+    constexpr bool MQ = decltype(mq)::value;
+    return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true, MQ> : decode_kernel<T, D, B, G, CH, W, false, MQ>;
   };
+  using vec = std::false_type;
   using ch4 = std::integral_constant<int, 4>;
   using ch8 = std::integral_constant<int, 8>;
   using ch16 = std::integral_constant<int, 16>;
@@ -623,12 +754,14 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   using w8 = std::integral_constant<int, 8>;
   const int part_tokens = a.partition_blocks * B;
   const bool mid = part_tokens >= kMidPartitionMin && part_tokens <= kShortPartitionTokens;
-  auto kernel = pick(ch4{}, w4{});
+  auto kernel = pick(ch4{}, w4{}, vec{});
   int waves = 4;
-  if constexpr (G > 4) {
-    kernel = part_tokens <= kShortPartitionTokens ? pick(ch8{}, w4{}) : pick(ch16{}, w4{});
+  if constexpr (matrix_core_scores(!std::is_same_v<T, float>, G, B)) {
+    kernel = pick(ch16{}, w4{}, std::true_type{});
+  } else if constexpr (G > 4) {
+    kernel = part_tokens <= kShortPartitionTokens ? pick(ch8{}, w4{}, vec{}) : pick(ch16{}, w4{}, vec{});
   } else if (mid) {
-    kernel = pick(ch8{}, w8{});
+    kernel = pick(ch8{}, w8{}, vec{});
     waves = 8;
   }
   hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream,
@@ -678,6 +811,10 @@ hipError_t dispatch_dim(const DecodeArgs &a, int group, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool decode_matrix_core_scores(int dtype, int group, int block_size) {
+  return matrix_core_scores(dtype == PA_BF16, group, block_size);
+}
 
 bool decode_supported(int dtype, int head_dim, int block_size, int group) {
   return (dtype == PA_F32 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&

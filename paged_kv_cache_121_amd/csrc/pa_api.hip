@@ -13,10 +13,14 @@ namespace {
 constexpr size_t kAlign = 256;
 // Automatic partitioning.  A call wants at least kMinWorkgroups workgroups
 // (two per compute unit) so every CU streams; few (sequence, KV head) pairs
-// are therefore split into equal partitions.  Batches with many pairs are
+// are therefore split into equal partitions.  The matrix-core decode kernel
+// (groups of 8) wants one workgroup per CU instead: measured on 8 x 32,768
+// tokens of a 64-head / 8-KV-head layer, 8,192-token partitions (256
+// workgroups) took 161 us against 171 us at 4,096 and 177 us at 2,048.  Batches with many pairs are
 // likely to mix short and long contexts, so their partitions are capped at
 // kSkewedPartitionTokens to keep one long sequence from becoming the tail.
 constexpr int64_t kMinWorkgroups = 512;
+constexpr int64_t kMinWorkgroupsMatrixCore = 256;
 constexpr int64_t kManyPairs = 1024;
 constexpr int kSkewedPartitionTokens = 2048;
 constexpr int kMinAutoPartitionTokens = 256;
@@ -73,9 +77,9 @@ int device_view(char *p, char **out) {
 
 int partition_unit(int block_size) { return block_size < 16 ? 16 : block_size; }
 
-int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
+int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len, int64_t min_wg) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  const int64_t want_parts = pairs >= kMinWorkgroups ? 1 : (kMinWorkgroups + pairs - 1) / pairs;
+  const int64_t want_parts = pairs >= min_wg ? 1 : (min_wg + pairs - 1) / pairs;
   int64_t part = (max_context_len + want_parts - 1) / want_parts;
   if (pairs >= kManyPairs && part > kSkewedPartitionTokens) part = kSkewedPartitionTokens;
   if (part < kMinAutoPartitionTokens) part = kMinAutoPartitionTokens;
@@ -92,9 +96,14 @@ int auto_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int ma
 }
 
 // Resolves the partition size in tokens, or returns a negative status.
-int resolve_partition(const PoolDesc &pool, int num_seqs, int max_context_len, int partition_size) {
-  if (partition_size == 0)
-    return auto_partition_tokens(pool.block_size, num_seqs, pool.num_kv_heads, max_context_len);
+int resolve_partition(const PoolDesc &pool, int num_seqs, int num_q_heads, int max_context_len,
+                      int partition_size) {
+  if (partition_size == 0) {
+    const int group = num_q_heads / pool.num_kv_heads;
+    const int64_t min_wg = decode_matrix_core_scores(pool.dtype, group, pool.block_size) ? kMinWorkgroupsMatrixCore
+                                                                                         : kMinWorkgroups;
+    return auto_partition_tokens(pool.block_size, num_seqs, pool.num_kv_heads, max_context_len, min_wg);
+  }
   if (partition_size < 0 || partition_size % partition_unit(pool.block_size) != 0) return PA_ERR_INVALID_ARG;
   if (partition_size / pool.block_size > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
   return partition_size;
@@ -194,7 +203,7 @@ int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t 
   const int st = check_pool(pool, &d);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
-  return resolve_partition(d, num_seqs, max_context_len, 0);
+  return resolve_partition(d, num_seqs, num_q_heads, max_context_len, 0);
 }
 
 size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
@@ -202,7 +211,7 @@ size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t n
   PoolDesc d;
   if (check_pool(pool, &d) != PA_OK) return 0;
   if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
-  const int part = resolve_partition(d, num_seqs, max_context_len, partition_size);
+  const int part = resolve_partition(d, num_seqs, num_q_heads, max_context_len, partition_size);
   if (part <= 0) return 0;
   const int parts = (max_context_len + part - 1) / part;
   if (parts <= 1) return 0;
@@ -228,7 +237,7 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
   if (num_seqs == 0) return PA_OK;
   if (q == nullptr || out == nullptr || block_tables == nullptr || context_lens == nullptr)
     return PA_ERR_INVALID_ARG;
-  const int part = resolve_partition(d, num_seqs, max_context_len, partition_size);
+  const int part = resolve_partition(d, num_seqs, num_q_heads, max_context_len, partition_size);
   if (part < 0) return part;
   const int parts = max_context_len == 0 ? 1 : (max_context_len + part - 1) / part;
   // one workgroup per (pair, partition), pairs rounded up to a multiple of 8

@@ -86,6 +86,9 @@ hipError_t launch_swap(const char *src_base, int64_t src_num_blocks, char *dst_b
 // Returns hipErrorInvalidValue when no kernel is built for the shape.
 hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int block_size, int group);
+// True where decode takes its scores from the matrix cores (bf16, groups of 8,
+// blocks of 16 tokens or more); the launch shape and partitioning follow it.
+bool decode_matrix_core_scores(int dtype, int group, int block_size);
 hipError_t launch_prefill(const PrefillArgs &args, hipStream_t stream);
 bool prefill_supported(int dtype, int head_dim, int block_size, int group);
 

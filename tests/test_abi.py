@@ -98,3 +98,25 @@ def test_host_side_argument_checks_without_a_gpu():
     need = lib.pa_decode_workspace_size(ref(good), 3, 4, 1024, 16)
     assert need > 0 and need % 256 == 0
     assert lib.pa_decode_workspace_size(ref(good), 3, 4, 16, 16) == 0
+
+
+def test_automatic_partition_follows_the_kernel_choice():
+    """8 sequences x 8 KV heads x 32,768 tokens: the matrix-core decode (bf16, groups of 8,
+    blocks of 16 or more) aims at one workgroup per compute unit (256: four partitions of
+    8,192 tokens), the vector kernels at two (512: eight of 4,096)."""
+    import paged_kv_cache_121_amd as pa
+    if not os.path.exists(pa.library_path()):
+        pytest.skip("libpa.so is not built here")
+    lib = pa.load_library()
+    ref = ctypes.byref
+    bf16 = pa.pa_pool(0x1000, 8192, 8, 32, 128, pa.PA_BF16)
+    assert lib.pa_decode_partition_size(ref(bf16), 8, 64, 32768) == 8192
+    assert lib.pa_decode_partition_size(ref(bf16), 8, 32, 32768) == 4096  # groups of 4
+    f32 = pa.pa_pool(0x1000, 8192, 8, 32, 128, pa.PA_F32)
+    assert lib.pa_decode_partition_size(ref(f32), 8, 64, 32768) == 4096
+    small = pa.pa_pool(0x1000, 8192, 8, 8, 128, pa.PA_BF16)  # 8-token blocks: vector kernel
+    assert lib.pa_decode_partition_size(ref(small), 8, 64, 32768) == 4096
+    # the workspace follows the same choice: 4 partitions x 8 x 64 rows
+    ws = lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 0)
+    assert ws == lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 8192)
+    assert ws < lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 4096)

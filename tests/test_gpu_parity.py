@@ -256,7 +256,8 @@ def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows():
 
 
 @pytest.mark.parametrize("block_size", [4, 8, 64, 128])
-@pytest.mark.parametrize("group,head_dim,dtype", [(4, 128, "bf16"), (8, 64, "f32"), (1, 128, "bf16")])
+@pytest.mark.parametrize("group,head_dim,dtype", [(4, 128, "bf16"), (8, 64, "f32"), (1, 128, "bf16"),
+                                             (8, 128, "bf16")])
 def test_decode_block_size_sweep(block_size, group, head_dim, dtype):
     # small blocks are taken 16 / B to a pipeline stage, large ones in 16-token stages;
     # lengths land inside a stage, on its edge and one past it
@@ -320,6 +321,44 @@ def test_decode_mixed_lengths_any_partition_count(hkv, group, partition_size):
     assert (got[5] == 0).all() and np.isnan(got[11]).all()
     keep = [s for s in range(len(lens)) if s not in (5, 11)]
     assert np.abs(got[keep] - want[keep]).max() <= ATOL
+
+
+@pytest.mark.parametrize("group,dtype,block_size,partition_size", [
+    (8, "bf16", 32, 0), (8, "bf16", 16, 256), (8, "bf16", 64, 128), (4, "bf16", 16, 0), (8, "f32", 16, 0),
+    (1, "bf16", 32, 512)])
+def test_decode_running_max_raised_mid_stream(group, dtype, block_size, partition_size):
+    # Keys along each KV head's mean query direction with a rising ramp (the running
+    # maximum climbs past the lazy-rescale threshold many times inside every stream and
+    # partition) and one spike token, so accumulators are rescaled mid-stream; random
+    # N(0,1) data never moves the maximum that far after the first stage.
+    from workloads import to_bf16_bits
+    hkv, D = 2, 128
+    lens = np.array([700, 333, 1030, 77, 16, 1], dtype=np.int64)
+    nb = int(sum(-(-L // block_size) for L in lens)) + 4
+    w = make_custom(name="rising-scores", seed=83 + group, dtype=dtype, num_blocks=nb, num_q_heads=hkv * group,
+                    num_kv_heads=hkv, head_dim=D, block_size=block_size, lengths=lens)
+    st = w.steps[0]
+    say(f"[rescale] G={group} {dtype} B={block_size} partition {partition_size}")
+    q = paged.to_f64(st.q)
+    pool = w.pool.copy()
+    rng = np.random.default_rng(5)
+    for s, L in enumerate(lens):
+        spike = int(rng.integers(0, L))
+        for h in range(hkv):
+            u = q[s, h * group:(h + 1) * group].sum(axis=0)
+            u /= np.linalg.norm(u)
+            # the group's top head ends 100 log2 units above where it starts; the spike adds 60
+            top = float((q[s, h * group:(h + 1) * group] @ u).max()) * float(w.scale) * np.log2(np.e)
+            for t in range(int(L)):
+                c = (100.0 * t / max(int(L) - 1, 1) + (60.0 if t == spike else 0.0)) / top
+                kv = (c * u + 0.05 * rng.standard_normal(D)).astype(np.float32)
+                b, o = paged.translate(w.block_tables[s], t, block_size)
+                pool[b, 0, h, o, :] = to_bf16_bits(kv) if dtype == "bf16" else kv
+    want = paged.decode_ref(pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    got = _decode_custom(w, pool, w.block_tables, st.context_lens, st.q, partition_size)
+    err = np.abs(got - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
 
 
 @pytest.mark.parametrize("group,dtype,partition_size", [(4, "bf16", 1024), (2, "f32", 2048), (4, "f32", 1536),
