@@ -30,6 +30,8 @@
 //   scores of heads sigma(l) ... sigma(l) + HPL - 1.  The query registers are
 //   loaded in a lane-dependent head order (register r holds head r ^ sigma(l))
 //   so every exchange step is uniform across lanes: no selects.
+//   Groups of 8 over bf16 pools take their scores from the matrix cores
+//   instead, with their own lane layout (described at the kernel, "MQ").
 // Softmax: scores are kept in log2 units (scale * log2 e folded in) and
 //   exponentiated with the hardware exp2.  The running max is raised only
 //   when a score exceeds it by more than kRescaleThreshold, so the rescale
