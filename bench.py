@@ -129,11 +129,14 @@ def settle(fn, ms: float = 100.0, cap: int = 3000):
 def block_manager_timing(w, steps: int = 32):
     """Host bookkeeping of one decode step with the native block manager (include/pa_blocks.h):
     every sequence of the workload appends one token (growth, copy-on-write check, slot), then
-    the batch's block tables are exported."""
+    the batch's block tables are exported.  The manager gets the workload's pool size or, where
+    that pool is full already (the 70B-shaped batch fills every block), the blocks its
+    sequences reach after the appended tokens plus the null block."""
     import paged_kv_cache_121_amd as pa
     lens = w.steps[0].context_lens
     S, B = len(lens), w.block_size
-    bm = pa.pa_bm_create(w.num_blocks, B, reserve_null_block=True)
+    need = int(sum(-(-(int(L) + steps) // B) for L in lens)) + 1
+    bm = pa.pa_bm_create(max(w.num_blocks, need), B, reserve_null_block=True)
     seqs = np.array([pa.pa_bm_add_sequence(bm) for _ in range(S)], dtype=np.int64)
     for i, L in enumerate(lens):
         pa.pa_bm_allocate_prompt(bm, int(seqs[i]), int(L) - 1)

@@ -87,6 +87,49 @@ def test_prefill_single_row_chunks_agree_with_decode():
     assert np.abs(got - dec).max() <= ATOL
 
 
+@pytest.mark.parametrize("group,block_size", [(4, 16), (8, 32), (1, 64)])
+def test_prefill_running_max_raised_mid_row(group, block_size):
+    # Queries near one direction per KV head and keys along it with a rising ramp plus a
+    # spike: every row's running maximum climbs past the lazy-rescale threshold tile after
+    # tile (causal rows see ever larger scores), so O and the row sums are rescaled
+    # mid-row; N(0,1) data never moves the maximum that far after the first tile.
+    from workloads import to_bf16_bits
+    hkv, D = 2, 128
+    ctx, chunk = [300, 200, 130], [300, 64, 1]
+    nb = sum(-(-L // block_size) for L in ctx) + 8
+    w = make_prefill_custom(name="prefill-rising", seed=61 + group, dtype="bf16", num_blocks=nb,
+                            num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=D, block_size=block_size,
+                            context_lens=ctx, chunk_lens=chunk)
+    say(f"[prefill rescale] G={group} B={block_size}")
+    rng = np.random.default_rng(9)
+    pool_np = oracle_pool(w).copy()
+    q = paged.to_f64(w.q).copy()  # [rows][Hq][D]
+    log2e = float(np.log2(np.e))
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        r0, r1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        spike = int(rng.integers(0, L))
+        for h in range(hkv):
+            u = rng.standard_normal(D)
+            u /= np.linalg.norm(u)
+            q[r0:r1, h * group:(h + 1) * group] = 3.0 * u + 0.3 * rng.standard_normal((r1 - r0, group, D))
+            # scores rise by about 100 log2 units over the context; the spike adds 60
+            per_unit = 3.0 * float(w.scale) * log2e
+            for t in range(L):
+                c = (100.0 * t / max(L - 1, 1) + (60.0 if t == spike else 0.0)) / per_unit
+                kv = (c * u + 0.05 * rng.standard_normal(D)).astype(np.float32)
+                b, o = paged.translate(w.block_tables[s], t, block_size)
+                pool_np[b, 0, h, o, :] = to_bf16_bits(kv)
+    qb = to_bf16_bits(q.astype(np.float32))
+    pool = pa.PagedKVPool(to_dev(pool_np, "bf16"))
+    got = pa.pa_prefill(pool, to_dev(qb, "bf16"), i32(w.query_start_loc), i32(w.context_lens),
+                        i32(w.block_tables), scale=float(w.scale), max_query_len=max(chunk)).cpu().numpy()
+    want = paged.prefill_ref(pool_np, qb, w.query_start_loc, w.context_lens, w.block_tables, float(w.scale))
+    err = np.abs(got.astype(np.float64) - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
+
+
 def test_prefill_padding_poison_is_never_read():
     w = make_prefill_custom(name="prefill-poison", seed=41, dtype="bf16", num_blocks=64, num_q_heads=8,
                             num_kv_heads=2, head_dim=128, block_size=16, context_lens=[45, 70],
