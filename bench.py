@@ -435,17 +435,19 @@ def d2d_copy_gbs(dev, nbytes: int = 2 << 30, reps: int = 10):
     return {"bytes": nbytes, "read_gbs": round(nbytes / t / 1e9, 1), "read_plus_write_gbs": round(2 * nbytes / t / 1e9, 1)}
 
 
-def other_workloads(dev, ks=(3, 4, 5), reps: int = 20):
+def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
     """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping, cache write,
-    decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak."""
+    decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak.  "4tp8" is one
+    GPU's share of workload 4 under 8-way tensor parallelism over heads (1 KV head, 8 query
+    heads, the same sequences): the shape one GPU of a sharded 70B layer runs."""
     import torch
 
     import paged_kv_cache_121_amd as pa
-    from workloads import CONFIG_NAMES, make_config
+    from workloads import CONFIG_NAMES, make_config, make_tp_share
     out = {}
     for k in ks:
         t0 = time.perf_counter()
-        w = make_config(k)
+        w = make_tp_share(8) if k == "4tp8" else make_config(k)
         bf = w.dtype == "bf16"
 
         def d(a):
@@ -495,11 +497,15 @@ def other_workloads(dev, ks=(3, 4, 5), reps: int = 20):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         kv = w.kv_bytes(0)
-        out[f"workload{k}"] = {"workload": CONFIG_NAMES[k], "steps": len(steps), "step_us": round(ms_step * 1e3, 2),
+        name = (CONFIG_NAMES[4] + "; one GPU's share at 8-way tensor parallelism: 1 KV head, 8 query heads"
+                if k == "4tp8" else CONFIG_NAMES[k])
+        out[f"workload{k}"] = {"workload": name, "steps": len(steps), "step_us": round(ms_step * 1e3, 2),
                                "decode_us": round(ms * 1e3, 2), "kv_bytes": kv,
                                "decode_gbs": round(kv / ms / 1e6, 1),
                                "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
-                               "kv_cache_policy": "keep cached" if keep else "stream"}
+                               "kv_cache_policy": "keep cached" if keep else "stream",
+                               "partition_size": pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads,
+                                                                             steps[0][8])}
         print(f"[bench] workload {k}: decode {out[f'workload{k}']['decode_us']} us "
               f"({out[f'workload{k}']['pct_hbm_peak']} %), step {out[f'workload{k}']['step_us']} us, "
               f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)

@@ -698,12 +698,18 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
 }
 
 // Combine the partitions of one (sequence, query head): D threads, one per
-// output element, partitions taken in order.
+// output element.  The maximum over partitions is taken in parallel (thread d
+// reads partitions d, d + D, ...; then a workgroup reduction); the weighted
+// sums run in partition order with the loads of 8 partitions issued together,
+// so the result depends only on logical positions.
 template <int D>
 __global__ void __launch_bounds__(D)
 combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
                const int32_t *__restrict__ context_lens, int num_q_heads, int max_context_len,
                int max_tokens_per_row, int part_tokens, int max_parts) {
+  constexpr int kCombineWaves = D / 64;
+  constexpr int kBatch = 8;
+  __shared__ float s_max[kCombineWaves];
   const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int np = partitions_of(context_lens[s], max_context_len, max_tokens_per_row, part_tokens);
   if (np <= 1) return;  // written by the decode kernel itself
@@ -711,10 +717,32 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
   const float *ml = ws_ml + row * max_parts * 2;
   const float *o = ws_o + row * max_parts * D + d;
   float M = kNegInf;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int p = d; p < np; p += D) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((d & 63) == 0) s_max[d >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) M = fmaxf(M, s_max[w]);
   const float Ms = M == kNegInf ? 0.0f : M;
   float num = 0.0f, den = 0.0f;
-  for (int p = 0; p < np; ++p) {
+  int p = 0;
+  for (; p + kBatch <= np; p += kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      mv[k] = ml[2 * (p + k)];
+      lv[k] = ml[2 * (p + k) + 1];
+      ov[k] = o[(int64_t)(p + k) * D];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float a = fast_exp2(mv[k] - Ms);
+      num += a * ov[k];
+      den += a * lv[k];
+    }
+  }
+  for (; p < np; ++p) {
     const float a = fast_exp2(ml[2 * p] - Ms);
     num += a * o[(int64_t)p * D];
     den += a * ml[2 * p + 1];

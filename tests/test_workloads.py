@@ -139,3 +139,16 @@ def test_full_size_workload_structure():
     assert w2.num_blocks == 38348 and w2.pool.dtype == np.uint16
     assert abs(w2.kv_bytes() - 1.083e9) < 0.01e9
     del w2
+
+
+def test_tensor_parallel_share_keeps_the_sequences():
+    """One GPU's share of the 70B-shaped workload at 8-way tensor parallelism: one KV head
+    serving eight query heads, with workload 4's sequences, lengths, block size and pool size."""
+    from workloads import make_tp_share
+    w = make_tp_share(8)
+    assert (w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size) == (8, 1, 128, 32)
+    assert w.pool.shape == (8192, 2, 1, 32, 128)
+    assert list(w.steps[0].context_lens) == [32768] * 8
+    # a permutation of the whole pool, as in workload 4
+    assert sorted(w.block_tables.ravel().tolist()) == list(range(8192))
+    assert w.kv_bytes(0) == 8 * 32768 * 2 * 1 * 128 * 2

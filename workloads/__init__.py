@@ -22,5 +22,6 @@ from .configs import (  # noqa: F401
     Workload,
     make_config,
     make_custom,
+    make_tp_share,
     to_bf16_bits,
 )

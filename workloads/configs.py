@@ -337,6 +337,17 @@ def make_config(k: int, small: bool = False) -> Workload:
     raise ValueError(f"no workload {k}")
 
 
+def make_tp_share(tp: int = 8) -> Workload:
+    """One GPU's share of the 70B-shaped long-context workload under tensor
+    parallelism over heads: the same 8 sequences of 32,768 tokens, 32-token
+    blocks and whole-pool permutation placement, with 8 / tp KV heads and
+    64 / tp query heads (tp = 8: one KV head serving eight query heads)."""
+    assert 8 % tp == 0
+    return make_custom(name=f"cfg4-70b-long-tp{tp}-share", seed=4 + 1000 * tp, dtype="bf16", num_blocks=8192,
+                       num_q_heads=64 // tp, num_kv_heads=8 // tp, head_dim=128, block_size=32,
+                       lengths=[32768] * 8, placement="permutation")
+
+
 # ---------------------------------------------------------------------------
 # prefill workloads
 # ---------------------------------------------------------------------------
