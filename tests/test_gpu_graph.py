@@ -23,7 +23,8 @@ def bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("k,partition_size", [(3, 0), (3, 64), (5, 0), (1, 32)])
+# workload 4 (groups of 8, bf16): the matrix-core decode kernel and its combine kernel
+@pytest.mark.parametrize("k,partition_size", [(3, 0), (3, 64), (5, 0), (1, 32), (4, 0), (4, 64)])
 def test_decode_step_replays_in_a_graph(k, partition_size):
     w = make_config(k, small=True)
     st = w.steps[0]
