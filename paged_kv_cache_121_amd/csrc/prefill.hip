@@ -496,12 +496,12 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       __builtin_amdgcn_s_setprio(1);
       qk(s_k[b], sc);
       __builtin_amdgcn_s_setprio(0);
-      // K(t+1) has arrived in s_k[1 - b], V(t+1) in the staging tile (issued a
-      // whole tile ago).  V(t+1) is converted here, between the score MFMAs and
-      // the softmax, so its LDS round trip overlaps this tile's work (2.7 %
-      // faster on chunked prefill than converting after P.V).  Nothing reads
-      // s_v[1 - b] during this tile: its last reader, P.V(t-1), ended before
-      // the previous barrier.
+      // Wait for tile t+1's loads (issued as this tile began: K into
+      // s_k[1 - b], V into the staging tile) and convert V(t+1) here, between
+      // the score MFMAs and the softmax, so its LDS round trip overlaps this
+      // tile's work (2.7 % faster on chunked prefill than converting after
+      // P.V).  Nothing reads s_v[1 - b] during this tile: its last reader,
+      // P.V(t-1), ended before the previous barrier.
       wait_lds_loads();
       if (t + 1 < ntiles) convert_v(s_v[1 - b], t + 1);
       row_max(t, sc);
