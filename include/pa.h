@@ -151,6 +151,12 @@ int pa_swap_blocks(const pa_pool *src, const pa_pool *dst, const int32_t *src_bl
 /*
  * Partition size (tokens) pa_decode uses when passed partition_size == 0.
  * Returns a positive multiple of the block size, or a negative pa_status.
+ * The automatic choice splits the sequences into equal partitions so a call
+ * has at least 512 workgroups (256, one per compute unit, where groups of 8
+ * over bf16 pools with blocks of 16 tokens or more take their scores from
+ * the matrix cores), caps partitions at 2,048 tokens in batches of 1,024 or
+ * more (sequence, KV head) pairs, and stays between 256 tokens and 512
+ * blocks.  It depends only on these arguments.
  */
 int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len);
