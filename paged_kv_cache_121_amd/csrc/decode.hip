@@ -221,8 +221,8 @@ __device__ __forceinline__ float head_value(const float (&v)[HPL], int hh) {
   }
 }
 
-// Matrix-core layout (groups of 8, bf16): the value lane hh of each 16-lane
-// row holds, in every lane of that row (DPP row_newbcast).
+// Matrix-core layout (groups of 8, bf16): every lane gets the value held by
+// lane hh of its 16-lane row (DPP row_newbcast).
 __device__ __forceinline__ float row_lane_value(float v, int hh) {
   switch (hh) {
     case 0: return dpp<0x150>(v);
@@ -454,13 +454,13 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
       const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
       const bool partial = tok0 + CH > L;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  #pragma unroll
+#pragma unroll
       for (int kc = 0; kc < KC; ++kc)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kc].w),
                                                       __builtin_bit_cast(bf16x8_t, qf[kc].w), acc, 0, 0, 0);
       // lane (row, col): scores of tokens tok0 + 4 row + i for head col
       float sc[4];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = (!partial || tok0 + 4 * row + i < L) ? acc[i] * scale_log2 : kNegInf;
       const float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       const float mn = fmaxf(m[0], cm);
@@ -469,31 +469,31 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
         const float alpha[1] = {upd ? fast_exp2(m[0] - mn) : 1.0f};
         lsum[0] *= alpha[0];
         m[0] = upd ? mn : m[0];
-  #pragma unroll
+#pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float a = head_bcast<G, HPL, MQ>(alpha, hh);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < EPL; ++e) o[hh][e] *= a;
         }
       }
       const float ms = m[0] == kNegInf ? 0.0f : m[0];
       float pr[4][1];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 4; ++i) pr[i][0] = fast_exp2(sc[i] - ms);
       lsum[0] += (pr[0][0] + pr[1][0]) + (pr[2][0] + pr[3][0]);
       // PV: load step i holds token 4 row + i in row `row`
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NS; ++i) {
         float v[EPL];
         widen<T, NW, EPL>(vf[i], v);
         if (partial && !(tok0 + 4 * row + i < L)) {
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < EPL; ++e) v[e] = 0.0f;
         }
-  #pragma unroll
+#pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float pb = head_bcast<G, HPL, MQ>(pr[i], hh);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pb, v[e], o[hh][e]);
         }
       }
