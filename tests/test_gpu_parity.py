@@ -236,9 +236,17 @@ def test_padding_poison_and_single_token_closed_form():
         assert np.array_equal(got[0, hq].astype(np.float64), v0[hq // G])
 
 
-def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows():
-    w = make_config(2, small=True)
-    say(f"[edge rows] {w.name}")
+@pytest.mark.parametrize("case,partition_size", [("cfg2", 0), ("g8", 0), ("g8", 64)])
+def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows(case, partition_size):
+    # cfg2: groups of 4 (vector kernel); g8: groups of 8 over bf16 with 32-token blocks
+    # (matrix-core kernel), in one partition and split into 64-token partitions
+    if case == "cfg2":
+        w = make_config(2, small=True)
+    else:
+        lens = [100, 300, 500, 77, 250, 33]
+        w = make_custom(name="edge-rows-g8", seed=97, dtype="bf16", num_blocks=sum(-(-L // 32) for L in lens) + 4,
+                        num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=32, lengths=lens)
+    say(f"[edge rows] {w.name} partition {partition_size}")
     st = w.steps[0]
     lens = st.context_lens.copy()
     tables = w.block_tables.copy()
@@ -247,7 +255,8 @@ def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows():
     tables[2, 1] = w.num_blocks + 5              # invalid block id inside the context: NaN
     n3 = -(-int(lens[3]) // w.block_size)
     tables[3, n3:] = -7                          # invalid ids beyond the context: never read
-    out = _decode_custom(w, w.pool, tables, lens, st.q, max_context_len=int(w.block_tables.shape[1] * 16))
+    out = _decode_custom(w, w.pool, tables, lens, st.q, partition_size,
+                         max_context_len=int(w.block_tables.shape[1] * w.block_size))
     assert (out[0] == 0).all()
     assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
     good = [s for s in range(w.num_seqs) if s not in (0, 1, 2)]
