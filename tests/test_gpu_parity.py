@@ -170,9 +170,10 @@ def test_cache_policy_flag_does_not_change_results(k):
     assert a.tobytes() == b.tobytes()
 
 
-@pytest.mark.parametrize("partition_size", [0, 32])
-def test_bit_identical_under_physical_relabeling(partition_size):
-    w = make_config(2, small=True)
+@pytest.mark.parametrize("k,partition_size", [(2, 0), (2, 32), (4, 0), (4, 64)])
+def test_bit_identical_under_physical_relabeling(k, partition_size):
+    # workload 4 (groups of 8): the matrix-core decode and its combine kernel
+    w = make_config(k, small=True)
     say(f"[relabel] {w.name} partition_size={partition_size}")
     st = w.steps[0]
     base = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, partition_size)
