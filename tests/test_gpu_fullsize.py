@@ -13,7 +13,7 @@ import torch
 
 import paged_kv_cache_121_amd as pa
 from oracle import accounting, paged
-from workloads import make_config
+from workloads import make_config, make_tp_share
 
 from _gpu_util import device_pool, i32, run_step, say, to_host
 
@@ -57,9 +57,11 @@ def sample_pairs(w, n, seed):
     return pairs
 
 
-@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("k", [2, 3, 4, "4tp8"])
 def test_fullsize_single_step(k):
-    w = make_config(k)
+    # "4tp8": one GPU's share of workload 4 at 8-way tensor parallelism (1 KV head, 8 query
+    # heads, 32 partitions per sequence), as the benchmark reports it
+    w = make_tp_share(8) if k == "4tp8" else make_config(k)
     pool = device_pool(w)
     part = pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads, int(w.steps[0].context_lens.max()))
     say(f"[fullsize] {w.name}: S={w.num_seqs} pool={w.num_blocks} blocks, partition={part} tokens")
@@ -71,7 +73,7 @@ def test_fullsize_single_step(k):
     st = w.steps[0]
     want_slots = paged.slot_mapping_ref(w.block_tables, st.write_seq, st.write_pos, w.block_size)
     np.testing.assert_array_equal(to_host(slots), want_slots)
-    check_samples(w, got, 0, sample_pairs(w, 8, 50 + k))
+    check_samples(w, got, 0, sample_pairs(w, 8, 50 + (5 if k == "4tp8" else k)))
     # the written rows landed bit for bit (every token of the step, K and V)
     pool_host = to_host(pool.data)
     for i, slot in enumerate(want_slots.tolist()):
