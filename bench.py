@@ -1,8 +1,9 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: slot mapping, cache
-write of the step's new tokens, then paged decode attention (copy-on-write
-block copies too when the workload has them).  Inputs are seeded synthetic
+One step = one pass of the whole path over one batch: slot mapping and cache
+write of the step's new tokens (one fused launch, pa_cache_write_at), then
+paged decode attention (copy-on-write block copies too when the workload has
+them).  Inputs are seeded synthetic
 data already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload 2] [--partition-size 0]
@@ -478,8 +479,7 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
             if not decode_only:
                 if ncow:
                     pa.pa_block_copy(pool, cs, cd)
-                slots = pa.pa_slot_mapping(pool, tables, ws, wp)
-                pa.pa_cache_write(pool, kn, vn, slots)
+                pa.pa_cache_write_at(pool, kn, vn, tables, ws, wp)
             return pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=mx, keep_cached=keep,
                                 out=out_buf, workspace=work)
 
@@ -689,8 +689,7 @@ def main():
     def step():
         if len(st.cow_src):
             pa.pa_block_copy(pool, cow_src, cow_dst)
-        pa.pa_slot_mapping(pool, tables, wseq, wpos, out=slots)
-        pa.pa_cache_write(pool, k_new, v_new, slots)
+        pa.pa_cache_write_at(pool, k_new, v_new, tables, wseq, wpos, slots_out=slots)
         decode()
 
     settle(step)

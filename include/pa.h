@@ -117,6 +117,25 @@ int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new,
                    const int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream);
 
 /*
+ * pa_slot_mapping and pa_cache_write in one launch: token i's slot is
+ * computed from (seq_ids[i], positions[i]) through block_tables exactly as
+ * pa_slot_mapping computes it, and its K and V rows are written there as
+ * pa_cache_write writes them (a token whose slot is -1 is skipped).  The
+ * pages' step writes the new token's K/V at its (block, offset) slot right
+ * after finding it ([TSS] "Finding a token"; [VIBE] vLLM procedure step 4);
+ * doing both in one kernel saves a launch per decode step.
+ *   k_new, v_new : [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *   block_tables, max_blocks_per_seq, num_seqs, seq_ids, positions : as for
+ *                  pa_slot_mapping.
+ *   slot_mapping : int64 [num_tokens] receiving the slots, or NULL.
+ * Same argument checks and errors as the two calls; two tokens with the
+ * same slot in one call is a caller error.
+ */
+int pa_cache_write_at(const pa_pool *pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, int32_t num_seqs, const int32_t *seq_ids,
+                      const int32_t *positions, int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/*
  * Whole-block copies for copy-on-write ([AINEW] copy-on-write passage;
  * [SALIV] "Advanced Memory Sharing and Copy-on-Write"; [VIBE] step 6 and
  * the block-copy kernel named in "Across GPUs").
@@ -222,7 +241,7 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
  *   block_tables    : int32 [num_seqs][max_blocks_per_seq].
  *   max_query_len   : host-known upper bound of n_s.
  * bf16 pools only (the contraction runs on the bf16 matrix cores); head_dim
- * 64 or 128; block size 16 or 32; group size 1, 2, 4 or 8.  Rows of a
+ * 64 or 128; block size 4, 8, 16, 32, 64 or 128; group size 1, 2, 4 or 8.  Rows of a
  * sequence whose bounds are inconsistent (n_s < 0, n_s > context length,
  * n_s > max_query_len, rows outside [0, total_tokens), context beyond the
  * table row) are NaN where they lie inside the output, and so are the rows

@@ -5,6 +5,7 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 
 * ``pa_slot_mapping(pool, block_tables, seq_ids, positions) -> slots``
 * ``pa_cache_write(pool, k_new, v_new, slot_mapping)``
+* ``pa_cache_write_at(pool, k_new, v_new, block_tables, seq_ids, positions)`` (both in one launch)
 * ``pa_block_copy(pool, src_blocks, dst_blocks)``
 * ``pa_swap_blocks(src_pool, dst_pool, src_blocks, dst_blocks)`` between a
   device pool and a pinned host pool (``HostKVPool``)
@@ -70,6 +71,7 @@ __all__ = [
     "pa_bm_host_free_queue",
     "pa_swap_blocks",
     "pa_cache_write",
+    "pa_cache_write_at",
     "pa_decode",
     "pa_decode_partition_size",
     "pa_decode_workspace_size",
@@ -116,6 +118,7 @@ _POOLP = ctypes.POINTER(pa_pool)
 _SIGNATURES = {
     "pa_slot_mapping": (_I32, [_POOLP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "pa_cache_write": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP]),
+    "pa_cache_write_at": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "pa_block_copy": (_I32, [_POOLP, _VP, _VP, _I32, _VP]),
     "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
     "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
@@ -328,6 +331,34 @@ def pa_cache_write(pool: PagedKVPool, k_new, v_new, slot_mapping) -> None:
     lib = load_library()
     _check(lib.pa_cache_write(pool.desc, _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(k_new.shape[0]),
                               _stream(k_new)), "pa_cache_write")
+
+
+def pa_cache_write_at(pool: PagedKVPool, k_new, v_new, block_tables, seq_ids, positions, slots_out=None):
+    """pa_slot_mapping and pa_cache_write in one launch: write each token's K/V ([T][Hkv][D],
+    pool dtype) at the slot of (seq_ids[i], positions[i]); tokens out of range are skipped.
+    ``slots_out`` (int64 [T]), when given, receives the slots.  Returns ``slots_out``."""
+    torch = _torch()
+    dev = pool.device
+    shape = None
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, name, pool.data.dtype, 3, dev)
+        _need(tuple(t.shape[1:]) == (pool.num_kv_heads, pool.head_dim), f"{name} must be [T][Hkv][D]")
+        shape = t.shape if shape is None else shape
+        _need(t.shape == shape, "k_new and v_new must have the same shape")
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2, dev)
+    _dev_tensor(seq_ids, "seq_ids", torch.int32, 1, dev)
+    _dev_tensor(positions, "positions", torch.int32, 1, dev)
+    n = int(k_new.shape[0])
+    _need(seq_ids.shape[0] == n and positions.shape[0] == n, "one seq id and one position per token")
+    if slots_out is not None:
+        _dev_tensor(slots_out, "slots_out", torch.int64, 1, dev)
+        _need(slots_out.shape[0] == n, "slots_out must have one slot per token")
+    lib = load_library()
+    _check(lib.pa_cache_write_at(pool.desc, _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+                                 int(block_tables.shape[1]), int(block_tables.shape[0]), _ptr(seq_ids),
+                                 _ptr(positions), _ptr(slots_out) if slots_out is not None else None, n,
+                                 _stream(k_new)), "pa_cache_write_at")
+    return slots_out
 
 
 def pa_block_copy(pool: PagedKVPool, src_blocks, dst_blocks) -> None:

@@ -11,38 +11,35 @@
 namespace pa {
 namespace {
 
-// slot = table[seq][pos / B] * B + pos % B  ([TSS] "Finding a token").  One
-// lane per token; any id or position outside its buffer yields -1.
+// slot = table[seq][pos / B] * B + pos % B  ([TSS] "Finding a token"); any
+// id or position outside its buffer yields -1.
+__device__ __forceinline__ int64_t token_slot(const int32_t *__restrict__ tables, int max_blocks_per_seq,
+                                              int num_seqs, int seq, int pos, int block_size, int64_t num_blocks) {
+  if (seq < 0 || seq >= num_seqs || pos < 0) return -1;
+  const int logical = pos / block_size;
+  if (logical >= max_blocks_per_seq) return -1;
+  const int64_t block = tables[(int64_t)seq * max_blocks_per_seq + logical];
+  if (block < 0 || block >= num_blocks) return -1;
+  return block * block_size + (pos - logical * block_size);
+}
+
+// One lane per token.
 __global__ void __launch_bounds__(256)
 slot_mapping_kernel(const int32_t *__restrict__ tables, int max_blocks_per_seq, int num_seqs,
                     const int32_t *__restrict__ seq_ids, const int32_t *__restrict__ positions,
                     int64_t *__restrict__ slots, int num_tokens, int block_size, int64_t num_blocks) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= num_tokens) return;
-  const int seq = seq_ids[i];
-  const int pos = positions[i];
-  int64_t slot = -1;
-  if (seq >= 0 && seq < num_seqs && pos >= 0) {
-    const int logical = pos / block_size;
-    if (logical < max_blocks_per_seq) {
-      const int64_t block = tables[(int64_t)seq * max_blocks_per_seq + logical];
-      if (block >= 0 && block < num_blocks) slot = block * block_size + (pos - logical * block_size);
-    }
-  }
-  slots[i] = slot;
+  slots[i] = token_slot(tables, max_blocks_per_seq, num_seqs, seq_ids[i], positions[i], block_size, num_blocks);
 }
 
-// One workgroup per written token.  Its 2 * Hkv rows (K then V, one per KV
-// head) are split into 16-byte words; word w of row r goes to
+// The workgroup's token's 2 * Hkv rows (K then V, one per KV head) are split
+// into 16-byte words; word w of row r goes to
 // pool[slot / B][r / Hkv][r % Hkv][slot % B][w * 16 bytes ...].
-__global__ void __launch_bounds__(256)
-cache_write_kernel(char *__restrict__ pool, int64_t num_slots, int num_kv_heads, int block_size,
-                   int64_t row_bytes, int64_t tile_bytes, int64_t block_bytes,
-                   const char *__restrict__ k_new, const char *__restrict__ v_new,
-                   const int64_t *__restrict__ slots) {
-  const int token = blockIdx.x;
-  const int64_t slot = slots[token];
-  if (slot < 0 || slot >= num_slots) return;
+__device__ __forceinline__ void write_token_rows(char *__restrict__ pool, int num_kv_heads, int block_size,
+                                                 int64_t row_bytes, int64_t tile_bytes, int64_t block_bytes,
+                                                 const char *__restrict__ k_new, const char *__restrict__ v_new,
+                                                 int token, int64_t slot) {
   const int64_t block = slot / block_size;
   const int64_t offset = slot - block * block_size;
   const int words_per_row = (int)(row_bytes / 16);
@@ -57,6 +54,35 @@ cache_write_kernel(char *__restrict__ pool, int64_t num_slots, int num_kv_heads,
                 offset * row_bytes + word * 16;
     *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
   }
+}
+
+// One workgroup per written token, slot given.
+__global__ void __launch_bounds__(256)
+cache_write_kernel(char *__restrict__ pool, int64_t num_slots, int num_kv_heads, int block_size,
+                   int64_t row_bytes, int64_t tile_bytes, int64_t block_bytes,
+                   const char *__restrict__ k_new, const char *__restrict__ v_new,
+                   const int64_t *__restrict__ slots) {
+  const int token = blockIdx.x;
+  const int64_t slot = slots[token];
+  if (slot < 0 || slot >= num_slots) return;
+  write_token_rows(pool, num_kv_heads, block_size, row_bytes, tile_bytes, block_bytes, k_new, v_new, token, slot);
+}
+
+// One workgroup per written token, slot computed from (sequence, position)
+// through the table (the slot mapping and the write in one launch); the slot
+// is also stored when `slots` is not null.
+__global__ void __launch_bounds__(256)
+cache_write_at_kernel(char *__restrict__ pool, int num_kv_heads, int block_size, int64_t row_bytes,
+                      int64_t tile_bytes, int64_t block_bytes, const char *__restrict__ k_new,
+                      const char *__restrict__ v_new, const int32_t *__restrict__ tables, int max_blocks_per_seq,
+                      int num_seqs, const int32_t *__restrict__ seq_ids, const int32_t *__restrict__ positions,
+                      int64_t *__restrict__ slots, int64_t num_blocks) {
+  const int token = blockIdx.x;
+  const int64_t slot =
+      token_slot(tables, max_blocks_per_seq, num_seqs, seq_ids[token], positions[token], block_size, num_blocks);
+  if (slots != nullptr && threadIdx.x == 0) slots[token] = slot;
+  if (slot < 0) return;  // a valid slot lies below num_blocks * block_size
+  write_token_rows(pool, num_kv_heads, block_size, row_bytes, tile_bytes, block_bytes, k_new, v_new, token, slot);
 }
 
 // Grid (pairs, slices): each workgroup copies one 16 KiB slice of one block,
@@ -113,6 +139,18 @@ hipError_t launch_cache_write(const PoolDesc &pool, const void *k_new, const voi
                      pool.num_blocks * pool.block_size, pool.num_kv_heads, pool.block_size, pool.row_bytes,
                      pool.tile_bytes, pool.block_bytes, static_cast<const char *>(k_new),
                      static_cast<const char *>(v_new), slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write_at(const PoolDesc &pool, const void *k_new, const void *v_new,
+                                 const int32_t *tables, int max_blocks_per_seq, int num_seqs, const int32_t *seq_ids,
+                                 const int32_t *positions, int64_t *slots, int num_tokens, hipStream_t stream) {
+  const int words = (int)(2 * pool.num_kv_heads * pool.row_bytes / 16);
+  const int threads = words >= 256 ? 256 : ((words + 63) / 64) * 64;
+  hipLaunchKernelGGL(cache_write_at_kernel, dim3(num_tokens), dim3(threads), 0, stream, pool.base,
+                     pool.num_kv_heads, pool.block_size, pool.row_bytes, pool.tile_bytes, pool.block_bytes,
+                     static_cast<const char *>(k_new), static_cast<const char *>(v_new), tables,
+                     max_blocks_per_seq, num_seqs, seq_ids, positions, slots, pool.num_blocks);
   return hipGetLastError();
 }
 

@@ -167,6 +167,20 @@ int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new, co
   return status_of(launch_cache_write(d, k_new, v_new, slot_mapping, num_tokens, stream));
 }
 
+int pa_cache_write_at(const pa_pool *pool, const void *k_new, const void *v_new, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, int32_t num_seqs, const int32_t *seq_ids, const int32_t *positions,
+                      int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  PoolDesc d;
+  const int st = check_pool(pool, &d);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr || seq_ids == nullptr || positions == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && max_blocks_per_seq > 0 && block_tables == nullptr) return PA_ERR_INVALID_ARG;
+  return status_of(launch_cache_write_at(d, k_new, v_new, block_tables, max_blocks_per_seq, num_seqs, seq_ids,
+                                         positions, slot_mapping, num_tokens, stream));
+}
+
 int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks, int32_t num_pairs,
                   hipStream_t stream) {
   PoolDesc d;

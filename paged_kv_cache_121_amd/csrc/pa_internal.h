@@ -76,6 +76,9 @@ hipError_t launch_slot_mapping(const PoolDesc &pool, const int32_t *tables, int 
                                int64_t *slots, int num_tokens, hipStream_t stream);
 hipError_t launch_cache_write(const PoolDesc &pool, const void *k_new, const void *v_new,
                               const int64_t *slots, int num_tokens, hipStream_t stream);
+hipError_t launch_cache_write_at(const PoolDesc &pool, const void *k_new, const void *v_new,
+                                 const int32_t *tables, int max_blocks_per_seq, int num_seqs, const int32_t *seq_ids,
+                                 const int32_t *positions, int64_t *slots, int num_tokens, hipStream_t stream);
 hipError_t launch_block_copy(const PoolDesc &pool, const int32_t *src, const int32_t *dst, int num_pairs,
                              hipStream_t stream);
 // Whole-block copies from one pool to another of the same geometry (bases as

@@ -70,6 +70,13 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.pa_swap_blocks(ref(good), ref(other), 1, 1, 1, None) == -1
     assert lib.pa_swap_blocks(ref(good), ref(good), 1, 1, 1, None) == -1
     assert lib.pa_swap_blocks(ref(good), ref(good), None, None, 0, None) == 0
+    # slot computation + write in one call: null inputs, nothing to do, unsupported pool
+    assert lib.pa_cache_write_at(ref(good), None, 1, 1, 4, 3, 1, 1, None, 2, None) == -1
+    assert lib.pa_cache_write_at(ref(good), 1, 1, 1, 4, 3, None, 1, None, 2, None) == -1
+    assert lib.pa_cache_write_at(ref(good), None, None, None, 0, 0, None, None, None, 0, None) == 0
+    assert lib.pa_cache_write_at(ref(good), 1, 1, 1, -1, 3, 1, 1, None, 2, None) == -1
+    assert lib.pa_cache_write_at(ref(pa.pa_pool(0x1000, 16, 4, 16, 96, 0)), 1, 1, 1, 4, 3, 1, 1, None, 2,
+                                 None) == -2
     # null pool base, negative sizes
     assert lib.pa_block_copy(ref(pa.pa_pool(None, 16, 4, 16, 64, 0)), 1, 1, 1, None) == -1
     assert lib.pa_block_copy(ref(good), 1, 1, -1, None) == -1

@@ -24,11 +24,13 @@ def bits(t):
 
 
 # workload 4 (groups of 8, bf16): the matrix-core decode kernel and its combine kernel
-@pytest.mark.parametrize("k,partition_size", [(3, 0), (3, 64), (5, 0), (1, 32), (4, 0), (4, 64)])
-def test_decode_step_replays_in_a_graph(k, partition_size):
+# fused: the slot mapping and the cache write as one call (pa_cache_write_at)
+@pytest.mark.parametrize("k,partition_size,fused", [(3, 0, False), (3, 64, False), (5, 0, False), (1, 32, False),
+                                                    (4, 0, False), (4, 64, False), (3, 0, True), (4, 64, True)])
+def test_decode_step_replays_in_a_graph(k, partition_size, fused):
     w = make_config(k, small=True)
     st = w.steps[0]
-    say(f"[graph] {w.name} partition_size={partition_size} cow_pairs={len(st.cow_src)}")
+    say(f"[graph] {w.name} partition_size={partition_size} cow_pairs={len(st.cow_src)} fused={fused}")
     pool0 = to_dev(w.pool, w.dtype)
     pool = pa.PagedKVPool(pool0.clone())
     tables, seqs, pos, lens = i32(w.block_tables), i32(st.write_seq), i32(st.write_pos), i32(st.context_lens)
@@ -45,8 +47,11 @@ def test_decode_step_replays_in_a_graph(k, partition_size):
     def step():
         if len(st.cow_src):
             pa.pa_block_copy(pool, src, dst)
-        pa.pa_slot_mapping(pool, tables, seqs, pos, out=slots)
-        pa.pa_cache_write(pool, kn, vn, slots)
+        if fused:
+            pa.pa_cache_write_at(pool, kn, vn, tables, seqs, pos, slots_out=slots)
+        else:
+            pa.pa_slot_mapping(pool, tables, seqs, pos, out=slots)
+            pa.pa_cache_write(pool, kn, vn, slots)
         pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=mcl,
                      partition_size=partition_size, out=out, workspace=ws, keep_cached=keep)
 

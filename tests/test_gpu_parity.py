@@ -90,6 +90,67 @@ def test_cache_write_skips_negative_and_out_of_pool_slots():
     assert to_host(pool.data).tobytes() == want.tobytes()
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_cache_write_at_bit_exact_whole_pool(k):
+    # slot computation and write in one launch: the same slots and the same pool as the oracle
+    w = make_config(k, small=True)
+    say(f"[cache_write_at] {w.name}")
+    pool = device_pool(w)
+    st = w.steps[0]
+    if len(st.cow_src):
+        pa.pa_block_copy(pool, i32(st.cow_src), i32(st.cow_dst))
+    slots = torch.empty(len(st.write_pos), dtype=torch.int64, device=DEV)
+    pa.pa_cache_write_at(pool, to_dev(st.k_new, w.dtype), to_dev(st.v_new, w.dtype), i32(w.block_tables),
+                         i32(st.write_seq), i32(st.write_pos), slots_out=slots)
+    torch.cuda.synchronize()
+    want_slots, want_pool = oracle_step(w, w.pool, 0)
+    np.testing.assert_array_equal(to_host(slots), want_slots)
+    assert to_host(pool.data).tobytes() == want_pool.tobytes()
+
+
+def test_cache_write_at_skips_tokens_out_of_range():
+    # bad sequence ids, negative positions, positions past the table row and table entries
+    # outside the pool get slot -1 and write nothing; the others land bit for bit
+    w = make_config(2, small=True)
+    say("[cache_write_at skip] cfg2-small")
+    pool = device_pool(w)
+    S, width = w.block_tables.shape
+    tables = w.block_tables.copy()
+    tables[4, 0] = w.num_blocks + 3
+    rng = np.random.default_rng(23)
+    seq = rng.integers(0, S, size=40).astype(np.int32)
+    pos = rng.integers(0, width * w.block_size, size=40).astype(np.int32)
+    seq[:4] = [-1, S, 0, 4]
+    pos[:4] = [3, 3, -5, 2]          # token 3 lands in the invalid table entry of sequence 4
+    pos[4] = width * w.block_size
+    def slot_of(i):
+        if 0 <= seq[i] < S and 0 <= pos[i] < width * w.block_size:
+            if 0 <= int(tables[seq[i], pos[i] // w.block_size]) < w.num_blocks:
+                return int(paged.slot_mapping_ref(tables, [seq[i]], [pos[i]], w.block_size)[0])
+        return -1
+    # one token per slot (table rows are padded with block 0, so distinct positions can share
+    # one): drop later duplicates
+    seen, keep = set(), []
+    for i in range(40):
+        sl = slot_of(i)
+        if sl < 0 or sl not in seen:
+            seen.add(sl)
+            keep.append(i)
+    want = np.array([slot_of(i) for i in keep], dtype=np.int64)
+    seq, pos = seq[keep], pos[keep]
+    n = len(keep)
+    from workloads import to_bf16_bits
+    kk = to_bf16_bits(rng.standard_normal((n, 8, 128)).astype(np.float32))
+    vv = to_bf16_bits(rng.standard_normal((n, 8, 128)).astype(np.float32))
+    got_slots = pa.pa_cache_write_at(pool, to_dev(kk, "bf16"), to_dev(vv, "bf16"), i32(tables), i32(seq), i32(pos),
+                                     slots_out=torch.empty(n, dtype=torch.int64, device=DEV))
+    pa.pa_cache_write_at(pool, to_dev(kk, "bf16"), to_dev(vv, "bf16"), i32(tables), i32(seq), i32(pos))  # no slots out
+    torch.cuda.synchronize()
+    assert (want[:5] == -1).all() and (want >= 0).sum() > 20
+    np.testing.assert_array_equal(to_host(got_slots), want)
+    assert to_host(pool.data).tobytes() == paged.cache_write_ref(w.pool, kk, vv, want).tobytes()
+
+
 def test_block_copy_bit_exact_whole_pool():
     for k in (1, 2, 4):
         w = make_config(k, small=True)
