@@ -450,3 +450,39 @@ def test_decode_work_shapes_by_partition(group, dtype, partition_size):
     want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
     got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, partition_size)
     assert np.isfinite(got).all() and np.abs(got - want).max() <= ATOL
+
+
+# ------------------------------------------------------------------ seeded random shapes
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([4, 8, 16, 32, 64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    hkv = int(rng.integers(1, 4))
+    S = int(rng.integers(1, 9))
+    lens = np.clip(np.rint(rng.lognormal(np.log(150), 1.0, size=S)), 1, 1200).astype(np.int64)
+    unit = max(B, 16)
+    part = int(rng.choice([0, unit, 2 * unit, 4 * unit]))
+    keep = bool(rng.integers(0, 2))
+    return G, D, B, dtype, hkv, lens, part, keep
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_decode_seeded_random_shapes(seed):
+    # one seeded draw of every supported knob at a time: group, head dim, block size, dtype,
+    # KV heads, ragged lengths, partition size and cache policy, against the oracle
+    G, D, B, dtype, hkv, lens, part, keep = _random_case(1000 + seed)
+    nb = int(sum(-(-L // B) for L in lens)) + 3
+    w = make_custom(name=f"random-{seed}", seed=2000 + seed, dtype=dtype, num_blocks=nb, num_q_heads=hkv * G,
+                    num_kv_heads=hkv, head_dim=D, block_size=B, lengths=lens)
+    st = w.steps[0]
+    say(f"[random {seed}] G={G} D={D} B={B} {dtype} Hkv={hkv} S={len(lens)} max={lens.max()} "
+        f"partition={part} keep_cached={keep}")
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, part, keep_cached=keep)
+    err = np.abs(got - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
