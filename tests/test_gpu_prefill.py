@@ -193,3 +193,28 @@ def test_prefill_fullsize_sampled_rows(k):
             errs.append(np.abs(got[int(w.query_start_loc[s]) + i].astype(np.float64) - want[0]).max())
     say(f"    {len(errs)} sampled rows, max abs err {max(errs):.3e}")
     assert max(errs) <= ATOL
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_prefill_seeded_random_shapes(seed):
+    # one seeded draw of group, head dim, block size, KV heads, contexts and chunk lengths
+    # (whole prompts, chunks, single rows) at a time, against the oracle
+    rng = np.random.default_rng(3000 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([4, 8, 16, 32, 64, 128]))
+    hkv = int(rng.integers(1, 3))
+    S = int(rng.integers(1, 5))
+    ctx = [int(x) for x in rng.integers(1, 400, size=S)]
+    chunk = [int(rng.choice([c, max(1, c // 3), 1])) for c in ctx]
+    nb = sum(-(-L // B) for L in ctx) + 4
+    w = make_prefill_custom(name=f"prefill-random-{seed}", seed=4000 + seed, dtype="bf16", num_blocks=nb,
+                            num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=D, block_size=B, context_lens=ctx,
+                            chunk_lens=chunk)
+    say(f"[prefill random {seed}] G={G} D={D} B={B} Hkv={hkv} contexts {ctx} chunks {chunk}")
+    _, got = gpu_prefill(w)
+    want = paged.prefill_ref(oracle_pool(w), w.q, w.query_start_loc, w.context_lens, w.block_tables,
+                             float(w.scale))
+    err = np.abs(got.astype(np.float64) - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
