@@ -328,7 +328,7 @@ def test_zero_length_and_invalid_inputs_give_zeros_and_nan_rows(case, partition_
 
 @pytest.mark.parametrize("block_size", [4, 8, 64, 128])
 @pytest.mark.parametrize("group,head_dim,dtype", [(4, 128, "bf16"), (8, 64, "f32"), (1, 128, "bf16"),
-                                             (8, 128, "bf16")])
+                                             (8, 128, "bf16"), (8, 64, "bf16")])
 def test_decode_block_size_sweep(block_size, group, head_dim, dtype):
     # small blocks are taken 16 / B to a pipeline stage, large ones in 16-token stages;
     # lengths land inside a stage, on its edge and one past it
