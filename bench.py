@@ -437,13 +437,13 @@ def d2d_copy_gbs(dev, nbytes: int = 2 << 30, reps: int = 10):
 
 
 def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
-    """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping, cache write,
-    decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak.  Output and
-    workspace are allocated once, and the decode-only launches run back to back between one
-    pair of events (a call of 30 us is otherwise timed with the binding's per-call host work
-    in it).  "4tp8" is one
-    GPU's share of workload 4 under 8-way tensor parallelism over heads (1 KV head, 8 query
-    heads, the same sequences): the shape one GPU of a sharded 70B layer runs."""
+    """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping and cache write
+    in one launch, decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak.
+    Output and workspace are allocated once, and the decode-only launches run back to back
+    between one pair of events (a call of 30 us is otherwise timed with the binding's per-call
+    host work in it).  "4tp8" is one GPU's share of workload 4 under 8-way tensor parallelism
+    over heads (1 KV head, 8 query heads, the same sequences): the shape one GPU of a sharded
+    70B layer runs."""
     import torch
 
     import paged_kv_cache_121_amd as pa
@@ -471,7 +471,8 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
                           d(st.v_new), d(st.q), i32(st.context_lens), int(st.context_lens.max()), len(st.cow_src)))
         stream = torch.cuda.current_stream(dev)
         out_buf = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-        need = max(pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, st[8]) for st in steps)
+        need = max(pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, int(st.context_lens.max()))
+                   for st in w.steps)
         work = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
         def run(i, decode_only=False):
