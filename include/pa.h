@@ -28,6 +28,30 @@
  *     entry point states.
  *   - Calls that overlap on one stream run in order; calls on different
  *     streams that touch the same pool region race.
+ *
+ * Checked mode (environment variable PA_CHECK=1, read at every call):
+ *   before launching, an entry point copies the index arrays it was given
+ *   (slots, seq ids, positions, tables, lengths, copy pairs, query starts)
+ *   to the host, waits for them, and returns PA_ERR_INVALID_ARG without
+ *   launching anything when it finds
+ *     - a written slot outside the pool, or two tokens of one write with the
+ *       same slot ([TSS] "Finding a token": one slot per token);
+ *     - a token whose sequence id lies outside [0, num_seqs) or whose
+ *       position lies beyond its table row (a negative position is padding
+ *       and passes);
+ *     - a copy pair with an id outside its pool, two pairs with the same
+ *       destination, or (inside one pool) a destination that is also a
+ *       source ([AINEW] copy-on-write passage: the shared block is never
+ *       written in place);
+ *     - a context length that is negative, exceeds max_context_len or the
+ *       table row, or a table id outside [0, num_blocks) among the first
+ *       ceil(len / block_size) entries of a row that attention reads;
+ *     - prefill bounds that are inconsistent (see pa_prefill).
+ *   Checked mode synchronises the stream and allocates host memory, so it is
+ *   a debugging aid: under graph capture it returns PA_ERR_UNSUPPORTED.
+ *   Without it (the default) the kernels skip such entries or return NaN
+ *   rows, as each entry point states, and never touch memory outside the
+ *   described buffers.
  */
 #ifndef PA_H
 #define PA_H
@@ -111,7 +135,8 @@ int pa_slot_mapping(const pa_pool *pool, const int32_t *block_tables, int32_t ma
  * pool[slot / B][0][h][slot % B][:] = k_new[i][h][:] and likewise V at index
  * 1, for every head, copied bit for bit.  Negative slots and slots at or
  * beyond num_blocks * block_size are skipped.  Two tokens with the same slot
- * in one call is a caller error (which one lands is unspecified).
+ * in one call is a caller error (which one lands is unspecified; checked
+ * mode refuses it).
  */
 int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new,
                    const int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream);
@@ -129,7 +154,7 @@ int pa_cache_write(const pa_pool *pool, const void *k_new, const void *v_new,
  *                  pa_slot_mapping.
  *   slot_mapping : int64 [num_tokens] receiving the slots, or NULL.
  * Same argument checks and errors as the two calls; two tokens with the
- * same slot in one call is a caller error.
+ * same slot in one call is a caller error (refused in checked mode).
  */
 int pa_cache_write_at(const pa_pool *pool, const void *k_new, const void *v_new, const int32_t *block_tables,
                       int32_t max_blocks_per_seq, int32_t num_seqs, const int32_t *seq_ids,
@@ -143,7 +168,7 @@ int pa_cache_write_at(const pa_pool *pool, const void *k_new, const void *v_new,
  * pool[dst[j]] = pool[src[j]] for every pair: K and V, every head, every
  * slot.  A pair with an id outside [0, num_blocks) is skipped.  Destinations
  * must be distinct and must not appear among the sources (else the result
- * is unspecified).
+ * is unspecified; checked mode refuses such pairs).
  */
 int pa_block_copy(const pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks,
                   int32_t num_pairs, hipStream_t stream);
@@ -181,12 +206,18 @@ int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t 
                                  int32_t max_context_len);
 
 /*
- * Device workspace bytes pa_decode needs for these arguments (0 when every
- * sequence fits one partition).  Returns 0 for invalid arguments too; the
- * decode call itself reports those.
+ * Device workspace bytes pa_decode needs for these arguments: 0 when every
+ * sequence fits one partition (no workspace needed), or a negative
+ * pa_status for arguments pa_decode would refuse (a bad pool, negative
+ * sizes, num_q_heads not a multiple of num_kv_heads, a partition_size that
+ * is not a multiple of max(block_size, 16) or exceeds 512 blocks).  The pool
+ * descriptor stands for the separate KV-head count and head size of a plain
+ * shape signature (it also fixes the block size, which the automatic
+ * partition depends on), and partition_size is the one pa_decode will get,
+ * since the partial results grow with the number of partitions.
  */
-size_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
-                                int32_t max_context_len, int32_t partition_size);
+int64_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size);
 
 /*
  * One decode step of paged attention ([VIBE] step 5: the kernel fetches key

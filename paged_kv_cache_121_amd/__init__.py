@@ -121,7 +121,7 @@ _SIGNATURES = {
     "pa_cache_write_at": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "pa_block_copy": (_I32, [_POOLP, _VP, _VP, _I32, _VP]),
     "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
-    "pa_decode_workspace_size": (_SZ, [_POOLP, _I32, _I32, _I32, _I32]),
+    "pa_decode_workspace_size": (_I64, [_POOLP, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
     "pa_prefill": (_I32, [_POOLP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
@@ -381,17 +381,27 @@ def pa_decode_partition_size(pool: PagedKVPool, num_seqs: int, num_q_heads: int,
 
 def pa_decode_workspace_size(pool: PagedKVPool, num_seqs: int, num_q_heads: int, max_context_len: int,
                              partition_size: int = 0) -> int:
-    return int(load_library().pa_decode_workspace_size(pool.desc, num_seqs, num_q_heads, max_context_len,
-                                                       partition_size))
+    r = int(load_library().pa_decode_workspace_size(pool.desc, num_seqs, num_q_heads, max_context_len,
+                                                    partition_size))
+    _check(min(r, 0), "pa_decode_workspace_size")
+    return r
 
 
 _workspaces: dict = {}
 
 
-def _workspace(device, nbytes: int):
-    """Scratch of at least ``nbytes`` per device, reused across calls (one stream)."""
+def _workspace(device, stream: ctypes.c_void_p, nbytes: int):
+    """Scratch of at least ``nbytes`` for one (device, stream) pair, reused by later calls on
+    that stream (calls on one stream never overlap; calls on two streams get two buffers).
+
+    Refused while the stream is being captured into a graph: a larger later request
+    replaces (frees) the cached buffer, which a replayed graph would still write, so a
+    captured call must be given a workspace that outlives the graph."""
     torch = _torch()
-    key = str(device)
+    if torch.cuda.is_current_stream_capturing():
+        raise ValueError("pa_decode under graph capture needs an explicit workspace "
+                         "(pa_decode_workspace_size bytes that outlive the graph)")
+    key = (str(device), stream.value)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -407,7 +417,9 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
     ``max_context_len`` defaults to the table width times the block size (a
     bound known without reading ``context_lens`` back from the device).
     ``keep_cached=True`` passes PA_DECODE_KEEP_CACHED (batches whose
-    sequences share physical blocks).
+    sequences share physical blocks).  Without ``workspace`` the split-context
+    partials go to a buffer cached per (device, stream); under graph capture
+    pass ``workspace`` explicitly.
     """
     torch = _torch()
     dev = pool.device
@@ -426,15 +438,17 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
     _dev_tensor(out, "out", torch.float32, 3, dev)
     _need(tuple(out.shape) == (S, Hq, D), "out must be [S][Hq][D]")
     need = pa_decode_workspace_size(pool, S, Hq, max_context_len, partition_size)
+    stream = _stream(q)
     if workspace is None:
-        ws = _workspace(dev, need) if need else None
+        ws = _workspace(dev, stream, need) if need else None
     else:
         ws = _dev_tensor(workspace, "workspace", torch.uint8, 1, dev)
     lib = load_library()
+    flags = PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM
     _check(lib.pa_decode(pool.desc, _ptr(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
-                         _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size),
-                         PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM, _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
-                         _stream(q)), "pa_decode")
+                         _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size), flags,
+                         _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, stream),
+           "pa_decode")
     return out
 
 

@@ -54,20 +54,12 @@
 namespace pa {
 namespace {
 
-#ifndef PA_DECODE_PREFETCH
-#define PA_DECODE_PREFETCH 1
-#endif
-
 // Partitions of kMidPartitionMin..kShortPartitionTokens tokens (mixed batches
 // of many pairs) take 8-wave workgroups and 8-token stages; groups of 8 take
 // 8-token stages up to kShortPartitionTokens.
 constexpr int kShortPartitionTokens = 2048;
 constexpr int kMidPartitionMin = 1024;
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup L is dispatched to XCD L % 8
-// Chunks in flight ahead of the one being processed.  Measured on the
-// Qwen3-8B batch-64 layer: 1 ahead already hides the latency (2 ahead was
-// 3 % slower, it costs 20 more VGPRs).
-constexpr int kPrefetch = PA_DECODE_PREFETCH;
 constexpr float kRescaleThreshold = 8.0f;     // log2 units the running max may lag
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -581,48 +573,23 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // the end re-reads the last chunk, an L2 hit), so the compiler's wait
   // counts at each use cover exactly the loads issued before it: each
   // process() waits for its own chunk while the next one is in flight.
-  if constexpr (kPrefetch == 1) {
-    if (nch > 0) {
-      Frag<KW> kA[KN];
-      Frag<NW> vA[NS];
-      Frag<KW> kB[KN];
-      Frag<NW> vB[NS];
-      const int last = nch - 1;
-      issue(0, kA, vA);
-      int ci = 0;
-      for (; ci < last; ci += 2) {
-        issue(ci + 1, kB, vB);
-        process(ci, kA, vA);
-        issue(min(ci + 2, last), kA, vA);
-        process(ci + 1, kB, vB);
-      }
-      if (ci == last) process(ci, kA, vA);
+  // One chunk is in flight ahead of the one being processed (measured on the
+  // Qwen3-8B batch-64 layer: two ahead was 3 % slower and cost 20 more VGPRs).
+  if (nch > 0) {
+    Frag<KW> kA[KN];
+    Frag<NW> vA[NS];
+    Frag<KW> kB[KN];
+    Frag<NW> vB[NS];
+    const int last = nch - 1;
+    issue(0, kA, vA);
+    int ci = 0;
+    for (; ci < last; ci += 2) {
+      issue(ci + 1, kB, vB);
+      process(ci, kA, vA);
+      issue(min(ci + 2, last), kA, vA);
+      process(ci + 1, kB, vB);
     }
-  } else {
-    static_assert(kPrefetch == 2, "prefetch depth 1 or 2");
-    // three buffers, two chunks in flight while one is processed
-    if (nch > 0) {
-      Frag<KW> kA[KN];
-      Frag<NW> vA[NS];
-      Frag<KW> kB[KN];
-      Frag<NW> vB[NS];
-      Frag<KW> kC[KN];
-      Frag<NW> vC[NS];
-      const int last = nch - 1;
-      issue(0, kA, vA);
-      issue(min(1, last), kB, vB);
-      int ci = 0;
-      for (; ci + 2 <= last; ci += 3) {
-        issue(ci + 2, kC, vC);
-        process(ci, kA, vA);
-        issue(min(ci + 3, last), kA, vA);
-        process(ci + 1, kB, vB);
-        issue(min(ci + 4, last), kB, vB);
-        process(ci + 2, kC, vC);
-      }
-      if (ci <= last) process(ci, kA, vA);
-      if (ci + 1 <= last) process(ci + 1, kB, vB);
-    }
+    if (ci == last) process(ci, kA, vA);
   }
 
   // ---- merge the four row streams of this wave (partners lane ^ 16, lane ^ 32)

@@ -105,6 +105,32 @@ def test_host_side_argument_checks_without_a_gpu():
     need = lib.pa_decode_workspace_size(ref(good), 3, 4, 1024, 16)
     assert need > 0 and need % 256 == 0
     assert lib.pa_decode_workspace_size(ref(good), 3, 4, 16, 16) == 0
+    assert lib.pa_decode_workspace_size(ref(good), 0, 4, 1024, 16) == 0   # nothing to do
+    # invalid arguments are a negative status, not "no workspace needed"
+    assert lib.pa_decode_workspace_size(ref(good), 3, 4, 1024, 24) == -1  # not a multiple of 16
+    assert lib.pa_decode_workspace_size(ref(good), 3, 6, 1024, 16) == -1  # Hq not a multiple of Hkv
+    assert lib.pa_decode_workspace_size(ref(good), -1, 4, 1024, 16) == -1
+    assert lib.pa_decode_workspace_size(ref(pa.pa_pool(0x1000, 16, 4, 12, 64, 0)), 3, 4, 1024, 16) == -2
+    assert lib.pa_decode_workspace_size(ref(good), 3, 4, 1 << 20, 16 * 513) == -2  # over 512 blocks
+
+
+def test_checked_mode_leaves_scalar_errors_and_no_ops_on_the_host(monkeypatch):
+    """With PA_CHECK=1 the scalar checks still come first and zero-work calls touch nothing, so
+    no device copy is attempted for them (these fake addresses would fault)."""
+    import paged_kv_cache_121_amd as pa
+    if not os.path.exists(pa.library_path()):
+        pytest.skip("libpa.so is not built here")
+    monkeypatch.setenv("PA_CHECK", "1")
+    lib = pa.load_library()
+    ref = ctypes.byref
+    good = pa.pa_pool(0x1000, 16, 4, 16, 64, pa.PA_F32)
+    assert lib.pa_cache_write(ref(pa.pa_pool(0x1000, 16, 4, 12, 64, 0)), 1, 1, 1, 1, None) == -2
+    assert lib.pa_cache_write(ref(good), None, None, None, 0, None) == 0
+    assert lib.pa_block_copy(ref(good), None, None, 0, None) == 0
+    assert lib.pa_block_copy(ref(good), 1, 1, -1, None) == -1
+    assert lib.pa_decode(ref(good), 1, 1, 1, 4, 1, 3, 6, 0.1, 48, 0, 0, None, 0, None) == -1
+    assert lib.pa_decode(ref(good), 1, 1, 1, 64, 1, 3, 4, 0.1, 1024, 16, 0, None, 0, None) == -3
+    assert lib.pa_prefill(ref(good), 1, 1, 1, 1, 1, 4, 3, 4, 10, 10, 0.1, None) == -2
 
 
 def test_automatic_partition_follows_the_kernel_choice():
@@ -127,3 +153,24 @@ def test_automatic_partition_follows_the_kernel_choice():
     ws = lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 0)
     assert ws == lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 8192)
     assert ws < lib.pa_decode_workspace_size(ref(bf16), 8, 64, 32768, 4096)
+
+
+def test_implicit_workspace_is_per_stream_and_refused_under_capture(monkeypatch):
+    """The binding's cached decode workspace: one buffer per (device, stream), so calls on two
+    streams never share it; refused while a graph is being captured (a later, larger request
+    would free the buffer a replayed graph still writes)."""
+    import torch
+
+    import paged_kv_cache_121_amd as pa
+    monkeypatch.setattr(pa, "_workspaces", {})
+    capturing = [False]
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: capturing[0])
+    a = pa._workspace("cpu", ctypes.c_void_p(0x10), 100)
+    assert pa._workspace("cpu", ctypes.c_void_p(0x10), 50) is a
+    b = pa._workspace("cpu", ctypes.c_void_p(0x20), 100)
+    assert b is not a and b.data_ptr() != a.data_ptr()
+    big = pa._workspace("cpu", ctypes.c_void_p(0x10), 4 << 20)
+    assert big is not a and big.numel() >= 4 << 20
+    capturing[0] = True
+    with pytest.raises(ValueError, match="graph capture"):
+        pa._workspace("cpu", ctypes.c_void_p(0x10), 100)

@@ -235,6 +235,18 @@ def test_tss_capacity_and_sharing():
     assert round(100 * pool.num_in_use / g["cache_blocks"], 1) == g["shared_percent"]
 
 
+def test_tss_finding_a_token():
+    # token 53 with 16-token blocks: logical block 3, offset 5, and the slot is the physical
+    # block times the block size plus the offset, through whatever the table holds there
+    g = load("tss_numbers.json")["finding_a_token"]
+    B, t = g["block_size"], g["token"]
+    assert paged.logical_block_and_offset(t, B) == (g["logical_block"], g["offset"])
+    table = [40, 7, 1234, 88, 3]
+    assert paged.translate(table, t, B) == (88, g["offset"])
+    assert paged.slot_id(table, t, B) == 88 * B + g["offset"] == 1413
+    assert paged.slot_mapping_ref([table], [0], [t], B).tolist() == [1413]
+
+
 # ---------------------------------------------------------------- pool bookkeeping
 
 
