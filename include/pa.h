@@ -271,12 +271,17 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
  *   context_lens    : int32 [num_seqs], cached tokens (this chunk included).
  *   block_tables    : int32 [num_seqs][max_blocks_per_seq].
  *   max_query_len   : host-known upper bound of n_s.
- * bf16 pools only (the contraction runs on the bf16 matrix cores); head_dim
- * 64 or 128; block size 4, 8, 16, 32, 64 or 128; group size 1, 2, 4 or 8.  Rows of a
- * sequence whose bounds are inconsistent (n_s < 0, n_s > context length,
- * n_s > max_query_len, rows outside [0, total_tokens), context beyond the
- * table row) are NaN where they lie inside the output, and so are the rows
- * of a 64-row tile that read a table id outside [0, num_blocks).
+ * bf16 pools only: both contractions run on the bf16 matrix cores, V as
+ * stored over bf16's whole range and the probabilities as two bf16 parts
+ * (within 2^-15 of their fp32 values); head_dim 64 or 128; block size 4, 8,
+ * 16, 32, 64 or 128; group size 1, 2, 4 or 8.  Finite results need finite K
+ * and V in the context and |v| * context * 256 below the fp32 maximum (the
+ * unnormalised sums are fp32).  Every row of a sequence whose bounds are
+ * inconsistent (n_s < 0, n_s > context length, n_s > max_query_len, rows
+ * outside [0, total_tokens), context beyond the table row) is NaN where it
+ * lies inside the output, and so is every row of a row tile (256 / group
+ * tokens of one KV head's query heads) whose keys take a table id outside
+ * [0, num_blocks).
  */
 int pa_prefill(const pa_pool *pool, const void *q, float *out, const int32_t *query_start_loc,
                const int32_t *context_lens, const int32_t *block_tables, int32_t max_blocks_per_seq,

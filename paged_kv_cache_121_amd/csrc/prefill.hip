@@ -13,24 +13,27 @@
 // One workgroup of 8 waves takes 256 query rows of one KV head (32 per wave,
 // two 16-row groups sharing every K and V operand read): rows are (head of
 // the GQA group, token) pairs, head-major, so every row of the workgroup
-// reads the same K/V, and each K/V tile is loaded and converted once for 8
-// waves (one workgroup per CU at two waves per SIMD).  K/V tiles of 64 keys go from HBM straight into LDS
-// (global_load_lds_dwordx4, no registers on the way), double-buffered, and
-// each wave computes flash-attention style on its rows:
+// reads the same K/V, and each K/V tile is loaded once for 8 waves (one
+// workgroup per CU at two waves per SIMD).  K/V tiles of 64 keys go from HBM
+// straight into LDS (global_load_lds_dwordx4, no registers on the way),
+// double-buffered, and each wave computes flash-attention style on its rows:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; A = K rows from LDS (ds_read_b128,
 //                 XOR-swizzled rows so 16 rows hit 16 different bank groups),
 //                 B = Q^T held in registers.  The C layout of S^T gives every
 //                 lane one row and four consecutive keys per 16-key sub-tile.
-//   P V           v_mfma_f32_16x16x32_f16; A = P straight from those registers
-//                 (the contraction's key order is permuted: slots 0-3 of a
-//                 lane group are keys 4g..4g+3 of one sub-tile, slots 4-7 the
-//                 same keys of the next), V's operand built in the same order
-//                 with the LDS transpose read ds_read_b64_tr_b16.
-// Numerics: P is rounded to fp16 (relative 2^-11; bf16's 2^-9 could cost a
-// row over two keys more than 2e-3) and V is converted to fp16 on its way
-// into the V tile, exact for |v| < 65504 (larger values saturate).  The row
-// sums come from the matrix cores too, as P times a block of ones, so they
-// weigh exactly the rounded P the output uses.  Online softmax in log2 units
+//   P V           v_mfma_f32_16x16x32_bf16 twice, P = P_hi + P_lo; A = those
+//                 parts straight from the registers (the contraction's key
+//                 order is permuted: slots 0-3 of a lane group are keys
+//                 4g..4g+3 of one sub-tile, slots 4-7 the same keys of the
+//                 next), V's operand built in the same order from the stored
+//                 bf16 with the LDS transpose read ds_read_b64_tr_b16.
+// Numerics: V is used exactly as stored (bf16, its whole range).  P in fp32
+// is split into P_hi (P with its low 16 bits cleared, a bf16) and P_lo =
+// bf16(P - P_hi) (the difference is exact in fp32 and below 2^-7 P), so
+// P_hi + P_lo is within 2^-15 P of P; one bf16 part alone (2^-8) could cost
+// a row over two keys more than 2e-3.  The row sums come from the matrix
+// cores too, as P_hi + P_lo times a block of ones, so they weigh exactly the
+// P the output uses.  Online softmax in log2 units
 // with the hardware exp2; the scale multiplies inside the exp2 argument (one
 // fma) and the running maximum is taken on unscaled scores, raised lazily
 // (threshold 8) as in decode.  Workgroups take each (sequence, head) pair's
@@ -56,8 +59,8 @@ constexpr float kPfNegInf = -__builtin_inff();
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfRescaleThreshold = 8.0f;
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -125,7 +128,6 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   __shared__ __attribute__((aligned(16))) char s_v1[C::TILEB];
   char *const s_k[2] = {s_k0, s_k1};
   char *const s_v[2] = {s_v0, s_v1};
-  __shared__ __attribute__((aligned(16))) char s_vst[C::TILEB];  // V as loaded (bf16), before conversion
 
   // Work order: (sequence, KV head) pairs one after another, each pair's row
   // tiles heaviest first (causal rows late in a prompt see the most keys).
@@ -155,13 +157,18 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   auto row_token = [&](int r) __attribute__((always_inline)) { return qt * QT + r % QT; };
   const int64_t hq0 = (int64_t)h * G;
 
-  if (bad) {  // NaN rows for what this tile covers, inside the output
+  if (bad) {
+    // NaN rows for the tokens this tile covers, inside the output; the last
+    // row tile also takes every token past the grid's tiles (n_s may exceed
+    // max_query_len, which sized the grid)
     if (q0 < 0 || n <= 0) return;
-    for (int i = tid; i < kRows * D; i += kPfThreads) {
-      const int r = i / D, d = i % D;
-      const int64_t row = (int64_t)q0 + row_token(r);
-      if (row_token(r) < n && row < total_tokens)
-        out[(row * num_q_heads + hq0 + row_head(r)) * D + d] = __builtin_nanf("");
+    const int64_t lim = min((int64_t)n, (int64_t)total_tokens - q0);  // tokens inside the output
+    const int64_t t0 = (int64_t)qt * QT;
+    const int64_t t1 = qt == num_row_tiles - 1 ? lim : min(lim, t0 + QT);
+    for (int64_t i = tid; i < (t1 - t0) * G * D; i += kPfThreads) {
+      const int64_t tok = t0 + i / (G * D);
+      const int hd = (int)(i % (G * D));
+      out[((q0 + tok) * num_q_heads + hq0) * D + hd] = __builtin_nanf("");
     }
     return;
   }
@@ -220,24 +227,30 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 
   // K and V go straight from global memory into LDS (global_load_lds_dwordx4:
   // each instruction writes 1 KiB, lane l's 16 bytes at l * 16).  Instruction i
-  // of wave w fills tile rows RPI*(4i+w) .. +RPI-1; lane l writes slot l % NCH16
-  // of row RPI*(4i+w) + l / NCH16.  For K it loads the chunk the XOR swizzle
-  // puts in that slot; V lands unswizzled in a staging tile and is converted
-  // to fp16 into its swizzled tile by the same lane (convert_v).  Keys past the
-  // context are loaded from wherever their rows fall (the last block's tail,
-  // or block 0 past the table's used entries): their scores are masked before
-  // any use and convert_v writes their values as zeros, so whatever those rows
-  // hold never reaches the output.
+  // of wave w fills tile rows RPI*(8i+w) .. +RPI-1; lane l writes slot l % NCH16
+  // of row RPI*(8i+w) + l / NCH16, and loads the chunk its tile's swizzle puts
+  // in that slot (K: 16-byte XOR swizzle, V: v_lds8).  Keys past the context
+  // are loaded from wherever their rows fall (the last block's tail, or block
+  // 0 past the table's used entries): their scores are masked before any use
+  // and zero_v_tail overwrites their values with zeros (a zero probability
+  // times a NaN would still be NaN), so whatever those rows hold never
+  // reaches the output.
   constexpr int RPI = 1024 / C::ROWB;  // key rows per instruction
   const int dl_row = lane / C::NCH16, dl_slot = lane % C::NCH16;
-  // this lane's byte offset inside an instruction's RPI rows (K: swizzled chunk)
-  uint32_t lane_off_k[C::LOADS];
+  // The chunk that lands in LDS slot `slot` of tile row `row`: the inverse of
+  // k_lds (16-byte XOR by row % NCH16) or of v_lds8 (which moves 16-byte
+  // chunk c to slot c ^ 2 (row % (NCH8 / 4))).
+  auto src_chunk = [&](int row, int slot, bool is_v) __attribute__((always_inline)) {
+    return is_v ? slot ^ (2 * (row % (C::NCH8 / 4))) : slot ^ (row % C::NCH16);
+  };
+  // this lane's byte offset inside an instruction's RPI rows
+  uint32_t lane_off_k[C::LOADS], lane_off_v[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int row = RPI * (kPfWaves * i + wave) + dl_row;
-    lane_off_k[i] = dl_row * C::ROWB + ((dl_slot ^ (row % C::NCH16)) << 4);
+    lane_off_k[i] = dl_row * C::ROWB + (src_chunk(row, dl_slot, false) << 4);
+    lane_off_v[i] = dl_row * C::ROWB + (src_chunk(row, dl_slot, true) << 4);
   }
-  const uint32_t lane_off_v = dl_row * C::ROWB + (dl_slot << 4);
   // block ids of tile t (scalar loads; fetched a tile ahead of their use)
   auto fetch_ids = [&](int t, int (&ids)[NBT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -246,7 +259,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       ids[i] = __builtin_amdgcn_readfirstlane(jb < seq_blocks ? table_row[jb] : 0);
     }
   };
-  auto load_lds = [&](int t, const int (&ids)[NBT], int64_t part_off, bool swizzle, char *buf)
+  auto load_lds = [&](int t, const int (&ids)[NBT], int64_t part_off, bool is_v, char *buf)
                       __attribute__((always_inline)) {
     int blk[NBT];
 #pragma unroll
@@ -262,7 +275,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       // Every instruction's RPI rows lie in one block, so its address is a
       // uniform base (scalar registers) plus this lane's fixed offset.  Rows
       // past the context read whatever the block holds there: their scores
-      // are masked, and convert_v zeroes their values.
+      // are masked, and zero_v_tail zeroes their values.
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const int row0 = RPI * (kPfWaves * i + wave);  // uniform
@@ -281,7 +294,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
         const char *sbase = reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
-        const uint32_t off = swizzle ? lane_off_k[i] : lane_off_v;
+        const uint32_t off = is_v ? lane_off_v[i] : lane_off_k[i];
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(sbase + off),
                                          (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
                                          16, 0, 0);
@@ -293,7 +306,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const int row = RPI * (kPfWaves * i + wave) + dl_row;
-        const int chunk = swizzle ? dl_slot ^ (row % C::NCH16) : dl_slot;
+        const int chunk = src_chunk(row, dl_slot, is_v);
         const int src_row = min(row, last_row);
         const int slot = src_row / B;
         int b = blk[0];
@@ -306,24 +319,19 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
     }
   };
-  // V from the staging tile (this lane's own loads) to fp16 in its swizzled tile;
-  // exact for |v| < 65504 (bf16 keeps 8 significant bits, fp16 11)
-  // Rows of tile t past the context become zeros.
-  auto convert_v = [&](char *buf, int t) __attribute__((always_inline)) {
+  // Rows of V tile t past the context hold whatever their source rows held
+  // (padding may be NaN); each lane overwrites the 16 bytes its own loads put
+  // there with zeros.  Only the tile where the context ends has such rows
+  // (uniform test); call after this wave's loads of the tile have landed.
+  auto zero_v_tail = [&](char *buf, int t) __attribute__((always_inline)) {
     const int vrows = ctx - t * kKeys;  // rows of the tile inside the context (uniform)
+    if (vrows < kKeys) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int row = RPI * (kPfWaves * i + wave) + dl_row;
-      const u32x4_t x = *reinterpret_cast<const u32x4_t *>(&s_vst[(kPfWaves * i + wave) * 1024 + lane * 16]);
-      u32x4_t vh;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        vh[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x[w] << 16),
-                                                                        __uint_as_float(x[w] & 0xffff0000u)));
-      if (vrows < kKeys) {  // uniform: the context ends inside this tile
-        if (row >= vrows) vh = u32x4_t{0u, 0u, 0u, 0u};
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int row = RPI * (kPfWaves * i + wave) + dl_row;
+        if (row >= vrows)
+          *reinterpret_cast<u32x4_t *>(&buf[(kPfWaves * i + wave) * 1024 + lane * 16]) = u32x4_t{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4_t *>(&buf[v_lds8<D>(row, 2 * dl_slot)]) = vh;
     }
   };
   // The LDS writes of this wave's loads are done (a barrier after this publishes them).
@@ -340,9 +348,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) o[rg][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  f16x8_t ones;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.0f;
+  const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});  // bf16 1.0
 
   // Per-lane LDS byte offsets of the operand reads; sub-tile, key-step and
   // buffer offsets fold into the instructions' immediate offsets.
@@ -416,37 +422,51 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
     }
   };
-  // Softmax, second half, and O += P V(t): P = exp2(cs * s - m) in fp16 (the
-  // permuted key order), row sums P 1 and the V products on the matrix cores.
+  // Softmax, second half, and O += P V(t): P = exp2(cs * s - m) in fp32 (the
+  // permuted key order), split into bf16 parts P_hi + P_lo; row sums P 1 and
+  // the V products on the bf16 matrix cores, each part in turn.
   auto exp_pv = [&](const f32x4_t (&sacc)[kRG][4], const char *vt_lds) __attribute__((always_inline)) {
-    f16x8_t ph[kRG][2];
+    bf16x8_t ph[kRG][2], pl[kRG][2];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       const float nms = m[rg] == kPfNegInf ? 0.0f : -m[rg];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4_t hi, lo;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            ph[rg][ks][4 * half + jj] = (_Float16)pf_exp2(__builtin_fmaf(sacc[rg][2 * ks + half][jj], cs, nms));
+          for (int jp = 0; jp < 2; ++jp) {
+            // slots 4 half + 2 jp, +1: keys jj = 2 jp, 2 jp + 1 of sub-tile 2 ks + half
+            const float p0 = pf_exp2(__builtin_fmaf(sacc[rg][2 * ks + half][2 * jp], cs, nms));
+            const float p1 = pf_exp2(__builtin_fmaf(sacc[rg][2 * ks + half][2 * jp + 1], cs, nms));
+            const uint32_t b0 = __float_as_uint(p0) & 0xFFFF0000u, b1 = __float_as_uint(p1) & 0xFFFF0000u;
+            hi[2 * half + jp] = b1 | (b0 >> 16);
+            const bf16x2_t r = {(__bf16)(p0 - __uint_as_float(b0)), (__bf16)(p1 - __uint_as_float(b1))};
+            lo[2 * half + jp] = __builtin_bit_cast(uint32_t, r);
+          }
+        ph[rg][ks] = as_bf16x8(hi);
+        pl[rg][ks] = as_bf16x8(lo);
+      }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
+        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], ones, osum[rg], 0, 0, 0);
+      }
     }
     // V operands are read kVAhead steps before the MFMAs that use them, and
-    // the schedule is pinned to (2 reads of a later step, 2 MFMAs of this one)
+    // the schedule is pinned to (2 reads of a later step, 4 MFMAs of this one)
     // so the reads' latency overlaps the matrix work (left to itself the
-    // scheduler waits on each step's reads just before its MFMAs; 2 % slower).
+    // scheduler waits on each step's reads just before its MFMAs).
     constexpr int NS = 2 * C::NT;  // (nt, ks) steps
-    f16x8_t vq[kVAhead];
+    bf16x8_t vq[kVAhead];
     auto rdv = [&](int st) __attribute__((always_inline)) {
       const int nt = st / 2, ks = st % 2;
       const i16x4_t lo4 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
       const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4_t *)(vt_lds + v_base[nt] + (32 * ks + 16) * C::ROWB));
-      return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 #pragma unroll
     for (int st = 0; st < kVAhead; ++st) vq[st] = rdv(st);
@@ -454,34 +474,36 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const int nt = st / 2, ks = st % 2;
-      const f16x8_t vb = vq[st % kVAhead];
+      const bf16x8_t vb = vq[st % kVAhead];
       if (st + kVAhead < NS) vq[st % kVAhead] = rdv(st + kVAhead);
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg)
-        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
+        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg)
+        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb, o[rg][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRG, 0);  // MFMAs
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
   using buf0 = std::integral_constant<int, 0>;
   using buf1 = std::integral_constant<int, 1>;
-  // ---- double buffering.  Iteration t: S(t) from buffer t%2; convert V(t+1)
-  // (arrived in the staging tile) into tile t-1's V buffer; softmax(t), PV(t);
-  // barrier; start K(t+2) into tile t's K buffer and V(t+2) into the staging
-  // tile.
+  // ---- double buffering.  Iteration t: S(t), softmax(t) and PV(t) from
+  // buffers t%2; wait for tile t+1's loads (and zero its V rows past the
+  // context); barrier; start K(t+2) and V(t+2) into buffers t%2.
   int ids[NBT];
   fetch_ids(0, ids);
-  load_lds(0, ids, 0, true, s_k[0]);
-  load_lds(0, ids, kv_half, false, s_vst);
+  load_lds(0, ids, 0, false, s_k[0]);
+  load_lds(0, ids, kv_half, true, s_v[0]);
   wait_lds_loads();
-  convert_v(s_v[0], 0);
+  zero_v_tail(s_v[0], 0);
   __syncthreads();
   if (ntiles > 1) {
     fetch_ids(1, ids);
-    load_lds(1, ids, 0, true, s_k[1]);
-    load_lds(1, ids, kv_half, false, s_vst);
+    load_lds(1, ids, 0, false, s_k[1]);
+    load_lds(1, ids, kv_half, true, s_v[1]);
   }
   f32x4_t sc[kRG][4];
   // one tile step; the arithmetic is skipped (COMPUTE false) for tiles past
@@ -496,24 +518,18 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       __builtin_amdgcn_s_setprio(1);
       qk(s_k[b], sc);
       __builtin_amdgcn_s_setprio(0);
-      // Wait for tile t+1's loads (issued as this tile began: K into
-      // s_k[1 - b], V into the staging tile) and convert V(t+1) here, between
-      // the score MFMAs and the softmax, so its LDS round trip overlaps this
-      // tile's work (2.7 % faster on chunked prefill than converting after
-      // P.V).  Nothing reads s_v[1 - b] during this tile: its last reader,
-      // P.V(t-1), ended before the previous barrier.
-      wait_lds_loads();
-      if (t + 1 < ntiles) convert_v(s_v[1 - b], t + 1);
       row_max(t, sc);
       exp_pv(sc, s_v[b]);
-    } else {
-      wait_lds_loads();
-      if (t + 1 < ntiles) convert_v(s_v[1 - b], t + 1);
     }
+    // Tile t+1's loads (issued as this tile began, into buffers 1 - b) have
+    // had this tile's work to land; the barrier publishes them and tells
+    // every wave that buffers b are free again.
+    wait_lds_loads();
+    if (t + 1 < ntiles) zero_v_tail(s_v[1 - b], t + 1);
     __syncthreads();
     if (t + 2 < ntiles) {
-      load_lds(t + 2, ids, 0, true, s_k[b]);
-      load_lds(t + 2, ids, kv_half, false, s_vst);
+      load_lds(t + 2, ids, 0, false, s_k[b]);
+      load_lds(t + 2, ids, kv_half, true, s_v[b]);
     }
   };
   using yes = std::true_type;
