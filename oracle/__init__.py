@@ -18,6 +18,9 @@ cites step by step with no blocking, fusion or reordering:
                     cached blocks, hits capped at the prompt minus one.
 * ``swap``       -- swap-out / swap-in of sequence groups between the GPU
                     pool and a host pool (the copy pairs a swap needs).
+* ``parallel``   -- the decode oracle run per sequence in spawned worker
+                    processes (no arithmetic of its own; for full-size checks
+                    and the all-cores CPU baseline).
 
 Citation keys used in docstrings (page title, then section):
 
@@ -35,4 +38,4 @@ against values the pages print, brute force, closed forms or invariants,
 except where a docstring says "parity unpinned".
 """
 
-from . import accounting, alloc, paged, prefix, swap  # noqa: F401
+from . import accounting, alloc, paged, parallel, prefix, swap  # noqa: F401

@@ -1,10 +1,22 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times (automatic partitioning), checked against the oracle on sampled
-outputs that it computes one by one, plus whole-output properties.
+times (automatic partitioning, cache policy per workload), checked against
+the oracle on every output row and on the whole pool.
 
-For a sampled sequence the oracle rebuilds only that sequence's blocks from
-the generator's initial pool (copy-on-write sources included), replays its
-own writes for every step up to the checked one, and decodes.
+* Workloads 2, 3, 4 and one GPU's share of workload 4 at 8-way tensor
+  parallelism: one step (copy-on-write copies, slot mapping + cache write,
+  decode); every (sequence, query head) row is compared with the float64
+  oracle (``oracle.parallel`` runs the oracle's decode per sequence in
+  worker processes), and the whole pool after the step equals the oracle's
+  pool byte for byte.
+* Workload 5 (32 steps of write-then-decode with growth): every sequence at
+  the first and last step, a rotating eighth of them at the steps between;
+  the whole pool after the last step byte for byte.
+
+Writes go through ``pa_cache_write_at`` (slot computation and write in one
+launch, as the benchmark's step does) for workloads 2, 3 and the
+tensor-parallel share, and through ``pa_slot_mapping`` + ``pa_cache_write``
+for workload 4; workload 5 alternates between the two by step.  Bars:
+slots and pools bit-exact, attention max-abs error 2e-3.
 """
 
 import numpy as np
@@ -12,89 +24,107 @@ import pytest
 import torch
 
 import paged_kv_cache_121_amd as pa
-from oracle import accounting, paged
+from oracle import paged
+from oracle.parallel import run_tasks, sequence_task, worker_pool
 from workloads import make_config, make_tp_share
 
-from _gpu_util import device_pool, i32, run_step, say, to_host
+from _gpu_util import device_pool, i32, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
 ATOL = 2e-3
 
 
-def oracle_sampled(w, s, k, hq):
-    """Oracle output row (sequence s, query head hq) after step k of workload w."""
-    B = w.block_size
-    L = int(w.steps[k].context_lens[s])
-    row = [int(b) for b in w.block_tables[s, :accounting.blocks_needed(L, B)]]
-    st0 = w.steps[0]
-    cow = dict(zip(st0.cow_dst.tolist(), st0.cow_src.tolist()))
-    small = np.stack([w.pool[cow.get(b, b)] for b in row])   # the step-0 copies, done per block
-    table = np.arange(len(row), dtype=np.int32)[None, :]
-    for j in range(k + 1):
-        stj = w.steps[j]
-        pos = int(stj.write_pos[s])
-        slot = paged.slot_mapping_ref(table, [0], [pos], B)
-        small = paged.cache_write_ref(small, stj.k_new[s:s + 1], stj.v_new[s:s + 1], slot)
-    return paged.decode_one_ref(small, w.steps[k].q[s:s + 1], table, [L], float(w.scale), 0, hq)
+def gpu_step(w, pool, tables, k, fused: bool):
+    """Step k on the GPU; returns (slots, output)."""
+    st = w.steps[k]
+    if len(st.cow_src):
+        pa.pa_block_copy(pool, i32(st.cow_src), i32(st.cow_dst))
+    kn, vn = to_dev(st.k_new, w.dtype), to_dev(st.v_new, w.dtype)
+    if fused:
+        slots = torch.empty(len(st.write_pos), dtype=torch.int64, device=pool.device)
+        pa.pa_cache_write_at(pool, kn, vn, tables, i32(st.write_seq), i32(st.write_pos), slots_out=slots)
+    else:
+        slots = pa.pa_slot_mapping(pool, tables, i32(st.write_seq), i32(st.write_pos))
+        pa.pa_cache_write(pool, kn, vn, slots)
+    out = pa.pa_decode(pool, to_dev(st.q, w.dtype), tables, i32(st.context_lens), scale=float(w.scale),
+                       max_context_len=int(st.context_lens.max()),
+                       keep_cached=bool(w.meta.get("prefix_tokens")))
+    torch.cuda.synchronize()
+    return to_host(slots), out.cpu().numpy()
 
 
-def check_samples(w, out, k, samples):
-    errs = []
-    for s, hq in samples:
-        want = oracle_sampled(w, s, k, hq)
-        errs.append(np.abs(out[s, hq].astype(np.float64) - want).max())
-    say(f"    step {k}: {len(samples)} sampled rows, max abs err {max(errs):.3e}")
-    assert max(errs) <= ATOL
-
-
-def sample_pairs(w, n, seed):
-    rng = np.random.default_rng(seed)
-    lens = w.steps[0].context_lens
-    pairs = [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), w.num_q_heads - 1)]
-    while len(pairs) < n:
-        pairs.append((int(rng.integers(w.num_seqs)), int(rng.integers(w.num_q_heads))))
-    return pairs
+def compare_rows(got, want_rows, seqs, tag):
+    err = max(float(np.abs(got[s].astype(np.float64) - want).max()) for s, want in zip(seqs, want_rows))
+    say(f"    {tag}: {len(seqs)} sequences x {got.shape[1]} heads, every row: max abs err {err:.3e}")
+    assert err <= ATOL
 
 
 @pytest.mark.parametrize("k", [2, 3, 4, "4tp8"])
-def test_fullsize_single_step(k):
+def test_fullsize_single_step_every_row(k):
     # "4tp8": one GPU's share of workload 4 at 8-way tensor parallelism (1 KV head, 8 query
     # heads, 32 partitions per sequence), as the benchmark reports it
     w = make_tp_share(8) if k == "4tp8" else make_config(k)
+    fused = k != 4
     pool = device_pool(w)
     part = pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads, int(w.steps[0].context_lens.max()))
-    say(f"[fullsize] {w.name}: S={w.num_seqs} pool={w.num_blocks} blocks, partition={part} tokens")
+    say(f"[fullsize] {w.name}: S={w.num_seqs} pool={w.num_blocks} blocks, partition={part} tokens, "
+        f"{'pa_cache_write_at' if fused else 'pa_slot_mapping + pa_cache_write'}")
     tables = i32(w.block_tables)
-    slots, out = run_step(w, pool, tables, 0)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
+    slots, got = gpu_step(w, pool, tables, 0, fused)
     assert np.isfinite(got).all()
     st = w.steps[0]
+    # the oracle's step: copies, slots, write
+    pool_np = w.pool
+    if len(st.cow_src):
+        pool_np = paged.block_copy_ref(pool_np, st.cow_src, st.cow_dst)
     want_slots = paged.slot_mapping_ref(w.block_tables, st.write_seq, st.write_pos, w.block_size)
-    np.testing.assert_array_equal(to_host(slots), want_slots)
-    check_samples(w, got, 0, sample_pairs(w, 8, 50 + (5 if k == "4tp8" else k)))
-    # the written rows landed bit for bit (every token of the step, K and V)
-    pool_host = to_host(pool.data)
-    for i, slot in enumerate(want_slots.tolist()):
-        b, o = divmod(slot, w.block_size)
-        assert pool_host[b, 0, :, o].tobytes() == st.k_new[i].tobytes()
-        assert pool_host[b, 1, :, o].tobytes() == st.v_new[i].tobytes()
+    np.testing.assert_array_equal(slots, want_slots)
+    pool_np = paged.cache_write_ref(pool_np, st.k_new, st.v_new, want_slots)
+    same = np.array_equal(to_host(pool.data), pool_np)
+    say(f"    whole pool ({pool_np.nbytes / 1e9:.2f} GB) after the step bit-exact: {same}")
+    assert same
+    del pool
+    # every output row
+    seqs = list(range(w.num_seqs))
+    tasks = (sequence_task(pool_np, w.block_tables[s], int(st.context_lens[s]), st.q[s], float(w.scale))
+             for s in seqs)
+    compare_rows(got, run_tasks(tasks), seqs, "step 0")
 
 
 def test_fullsize_growth_workload_all_steps():
     w = make_config(5)
-    say(f"[fullsize] {w.name}: S={w.num_seqs} steps={len(w.steps)} "
-        f"tokens={int(w.steps[0].context_lens.sum())}")
+    n_steps = len(w.steps)
+    say(f"[fullsize] {w.name}: S={w.num_seqs} steps={n_steps} tokens={int(w.steps[0].context_lens.sum())}")
     pool = device_pool(w)
     tables = i32(w.block_tables)
-    pairs_all = sample_pairs(w, 16, 55)
-    for k in range(len(w.steps)):
-        _, out = run_step(w, pool, tables, k)
-        if k in (0, len(w.steps) - 1):
-            pairs = pairs_all
-        else:  # a rotating subset in between
-            pairs = pairs_all[k % 8::8]
-        got = out.cpu().numpy()
+    B = w.block_size
+    all_slots = []
+    workers = worker_pool()
+    for k in range(n_steps):
+        st = w.steps[k]
+        slots, got = gpu_step(w, pool, tables, k, fused=(k % 2 == 0))
+        want_slots = paged.slot_mapping_ref(w.block_tables, st.write_seq, st.write_pos, B)
+        np.testing.assert_array_equal(slots, want_slots)
+        all_slots.append(want_slots)
         assert np.isfinite(got).all()
-        check_samples(w, got, k, pairs)
+        seqs = list(range(w.num_seqs)) if k in (0, n_steps - 1) else list(range(k % 8, w.num_seqs, 8))
+        # each checked sequence: its blocks as generated, with its own writes of steps 0..k replayed
+        tasks = []
+        for s in seqs:
+            writes = (np.array([w.steps[j].write_pos[s] for j in range(k + 1)], dtype=np.int32),
+                      np.stack([w.steps[j].k_new[s] for j in range(k + 1)]),
+                      np.stack([w.steps[j].v_new[s] for j in range(k + 1)]))
+            tasks.append(sequence_task(w.pool, w.block_tables[s], int(st.context_lens[s]), st.q[s],
+                                       float(w.scale), writes))
+        compare_rows(got, run_tasks(tasks, pool=workers), seqs, f"step {k}")
+    workers.shutdown()
+    # the whole pool after the last step: every step wrote one new position of every
+    # sequence, so the writes of all steps land on distinct slots and apply in one call
+    slots = np.concatenate(all_slots)
+    assert len(np.unique(slots[slots >= 0])) == int((slots >= 0).sum())
+    pool_np = paged.cache_write_ref(w.pool, np.concatenate([st.k_new for st in w.steps]),
+                                    np.concatenate([st.v_new for st in w.steps]), slots)
+    same = np.array_equal(to_host(pool.data), pool_np)
+    say(f"    whole pool after {n_steps} steps bit-exact: {same}")
+    assert same

@@ -294,3 +294,24 @@ def test_chunked_prefill_matches_brute_force():
                 bf = brute_force_attention(q[row, h].astype(np.float64), kv[:pos + 1, 0, 0], kv[:pos + 1, 1, 0], 0.5)
                 np.testing.assert_allclose(out[row, h], bf, rtol=0, atol=1e-12)
             row += 1
+
+
+def test_parallel_runner_equals_the_whole_pool_oracle():
+    """oracle.parallel runs decode_ref per sequence on that sequence's blocks (identity table),
+    optionally after replaying its writes: the same numbers, bit for bit, as decode_ref and
+    cache_write_ref over the whole pool, in this process and in spawned workers."""
+    from oracle.parallel import run_tasks, sequence_task
+    from workloads import make_custom
+    w = make_custom(name="par", seed=11, dtype="bf16", num_blocks=64, num_q_heads=8, num_kv_heads=2,
+                    head_dim=64, block_size=16, lengths=[70, 1, 33, 16], num_steps=1)
+    st = w.steps[0]
+    slots = paged.slot_mapping_ref(w.block_tables, st.write_seq, st.write_pos, w.block_size)
+    after = paged.cache_write_ref(w.pool, st.k_new, st.v_new, slots)
+    want = paged.decode_ref(after, st.q, w.block_tables, st.context_lens, float(w.scale))
+    plain = [sequence_task(after, w.block_tables[s], int(st.context_lens[s]), st.q[s], float(w.scale))
+             for s in range(w.num_seqs)]
+    replay = [sequence_task(w.pool, w.block_tables[s], int(st.context_lens[s]), st.q[s], float(w.scale),
+                            (st.write_pos[s:s + 1], st.k_new[s:s + 1], st.v_new[s:s + 1]))
+              for s in range(w.num_seqs)]
+    for got in (run_tasks(plain, workers=1), run_tasks(replay, workers=1), run_tasks(replay, workers=2)):
+        assert all(np.array_equal(g, want[s]) for s, g in enumerate(got))
