@@ -256,6 +256,27 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
               int32_t flags, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode without allocation, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, kernels and results as pa_decode
+ * with no workspace arguments.  The split-context partials go to a static
+ * device array of the library, 32 MiB on each device it runs on, held until
+ * the process ends; a call whose partials need more (see
+ * pa_decode_workspace_size) returns PA_ERR_WORKSPACE and launches nothing.
+ * Every call on one device shares that array and leaves its contents behind
+ * (nothing in it needs clearing: each call writes every partial it reads), so
+ * calls that overlap in time on one device race -- calls on one stream never
+ * do.  `stream` must belong to the current device (PA_ERR_INVALID_ARG
+ * otherwise).  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); no call allocates, frees or synchronises.  Checked
+ * mode does not apply here (it allocates host memory).
+ */
+int pa_decode_noalloc(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
+                      int32_t flags, hipStream_t stream);
+
+/*
  * Prefill or chunked prefill: many query rows per sequence, causal
  * ([HRL] section 9, prefill computes a prompt's tokens together; [TSS]
  * "Next", chunked prefill takes a prompt a chunk at a time; [HRL] section 8

@@ -10,6 +10,8 @@ ABI declared in ``include/pa.h``.  Functions carry the C names:
 * ``pa_swap_blocks(src_pool, dst_pool, src_blocks, dst_blocks)`` between a
   device pool and a pinned host pool (``HostKVPool``)
 * ``pa_decode(pool, q, block_tables, context_lens, ...) -> out``
+* ``pa_decode_noalloc(pool, q, block_tables, context_lens, out, ...)`` (no
+  workspace: the partials go to the library's static device array)
 * ``pa_decode_workspace_size(...)``, ``pa_decode_partition_size(...)``
 * ``pa_prefill(pool, q, query_start_loc, context_lens, block_tables, ...) -> out``
 * the host block manager of ``include/pa_blocks.h``: ``pa_bm_create``,
@@ -73,6 +75,7 @@ __all__ = [
     "pa_cache_write",
     "pa_cache_write_at",
     "pa_decode",
+    "pa_decode_noalloc",
     "pa_decode_partition_size",
     "pa_decode_workspace_size",
     "pa_prefill",
@@ -123,6 +126,7 @@ _SIGNATURES = {
     "pa_decode_partition_size": (_I32, [_POOLP, _I32, _I32, _I32]),
     "pa_decode_workspace_size": (_I64, [_POOLP, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP, _SZ, _VP]),
+    "pa_decode_noalloc": (_I32, [_POOLP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _F32, _I32, _I32, _I32, _VP]),
     "pa_status_str": (ctypes.c_char_p, [_I32]),
     "pa_prefill": (_I32, [_POOLP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     # host block manager (include/pa_blocks.h)
@@ -449,6 +453,33 @@ def pa_decode(pool: PagedKVPool, q, block_tables, context_lens, scale: float | N
                          _ptr(context_lens), S, Hq, float(scale), int(max_context_len), int(partition_size), flags,
                          _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0, stream),
            "pa_decode")
+    return out
+
+
+def pa_decode_noalloc(pool: PagedKVPool, q, block_tables, context_lens, out, scale: float | None = None,
+                      max_context_len: int | None = None, partition_size: int = 0, keep_cached: bool = False):
+    """``pa_decode`` into a caller-given ``out`` with no workspace and no allocation: the
+    split-context partials go to the library's static per-device array (calls overlapping in
+    time on one device race; at most 32 MiB of partials)."""
+    torch = _torch()
+    dev = pool.device
+    _dev_tensor(q, "q", pool.data.dtype, 3, dev)
+    S, Hq, D = (int(x) for x in q.shape)
+    _need(D == pool.head_dim, "q head_dim must match the pool")
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2, dev)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(block_tables.shape[0] == S and context_lens.shape[0] == S, "one table row and length per sequence")
+    _dev_tensor(out, "out", torch.float32, 3, dev)
+    _need(tuple(out.shape) == (S, Hq, D), "out must be [S][Hq][D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_context_len is None:
+        max_context_len = int(block_tables.shape[1]) * pool.block_size
+    flags = PA_DECODE_KEEP_CACHED if keep_cached else PA_DECODE_STREAM
+    _check(load_library().pa_decode_noalloc(pool.desc, _ptr(q), _ptr(out), _ptr(block_tables),
+                                            int(block_tables.shape[1]), _ptr(context_lens), S, Hq, float(scale),
+                                            int(max_context_len), int(partition_size), flags, _stream(q)),
+           "pa_decode_noalloc")
     return out
 
 

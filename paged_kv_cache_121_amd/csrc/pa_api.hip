@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <unordered_set>
 #include <vector>
 
@@ -298,6 +299,49 @@ void bind_workspace(DecodeArgs *a, char *base) {
   a->ws_ml = reinterpret_cast<float *>(base + w.ml_off);
 }
 
+// ---- decode without allocation (pa_decode_noalloc): the split-context
+// partials go to this file-scope device array instead of a caller's
+// workspace.  Every device the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address is taken once
+// per device with hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+char *g_scratch_address[kMaxScratchDevices];  // per device; null until first taken
+
+// Device address of `scratch` on the current device, which must be the
+// stream's device.
+int scratch_address(hipStream_t stream, char **out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) {
+      (void)hipGetLastError();
+      return PA_ERR_INVALID_ARG;
+    }
+    if (sd != cur) return PA_ERR_INVALID_ARG;
+  }
+  if (cur < 0 || cur >= kMaxScratchDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_address[cur] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    g_scratch_address[cur] = static_cast<char *>(p);
+  }
+  *out = g_scratch_address[cur];
+  return PA_OK;
+}
+
 }  // namespace
 
 WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -469,6 +513,25 @@ int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *blo
     const int c = check_decode_inputs(a.pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                       max_context_len, stream);
     if (c != PA_OK) return c;
+  }
+  return status_of(launch_decode(a, stream));
+}
+
+int pa_decode_noalloc(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, float scale, int32_t max_context_len, int32_t partition_size,
+                      int32_t flags, hipStream_t stream) {
+  DecodeArgs a{};
+  size_t need = 0;
+  const int st = prepare_decode(pool, q, out, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                scale, max_context_len, partition_size, flags, &a, &need);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (need > kScratchBytes) return PA_ERR_WORKSPACE;
+  if (need > 0) {
+    char *ws = nullptr;
+    const int s2 = scratch_address(stream, &ws);
+    if (s2 != PA_OK) return s2;
+    bind_workspace(&a, ws);
   }
   return status_of(launch_decode(a, stream));
 }

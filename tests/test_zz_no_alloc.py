@@ -1,0 +1,92 @@
+"""pa_decode_noalloc through the C ABI: the allocation-free variant of
+pa_decode (split-context partials in the library's static per-device array)
+gives the same bits as pa_decode with a caller workspace, on two calls in a
+row (the second smaller, so it reuses what the first left in the array), and
+refuses a call whose partials exceed the array."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_121_amd as pa
+from oracle import paged
+from workloads import make_custom
+
+from _gpu_util import device_pool, i32, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+def noalloc(pool, q, tables, lens, scale, mcl, part, out):
+    """One call of the C entry point itself (ctypes), on torch's current stream."""
+    lib = pa.load_library()
+    S, Hq, _ = q.shape
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    return lib.pa_decode_noalloc(pool.desc, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(tables.data_ptr()), int(tables.shape[1]),
+                                 ctypes.c_void_p(lens.data_ptr()), int(S), int(Hq), float(scale), int(mcl),
+                                 int(part), 0, stream)
+
+
+@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("bf16", 8), ("f32", 2)])
+def test_noalloc_matches_pa_decode_on_two_calls(dtype, group):
+    cases = [  # (lengths, partition tokens): the second call is smaller
+        ([3000, 2500, 1, 2999, 777, 3000, 64, 1500], 512),
+        ([700, 33, 690], 256),
+    ]
+    for i, (lengths, part) in enumerate(cases):
+        w = make_custom(name=f"noalloc-{i}", seed=90 + i + 10 * group, dtype=dtype,
+                        num_blocks=sum(-(-L // 16) for L in lengths) + 8, num_q_heads=2 * group, num_kv_heads=2,
+                        head_dim=128, block_size=16, lengths=lengths)
+        st = w.steps[0]
+        pool = device_pool(w)
+        q, tables, lens = to_dev(st.q, w.dtype), i32(w.block_tables), i32(st.context_lens)
+        mcl = int(st.context_lens.max())
+        need = pa.pa_decode_workspace_size(pool, w.num_seqs, w.num_q_heads, mcl, part)
+        say(f"[noalloc] call {i + 1}: {w.dtype} G={group} S={w.num_seqs} partitions of {part}, "
+            f"partials {need} B")
+        assert need > 0  # the partials really go through the static array
+        out = torch.full((w.num_seqs, w.num_q_heads, w.head_dim), 7.0, device=pool.device)
+        assert noalloc(pool, q, tables, lens, w.scale, mcl, part, out) == 0
+        ref = pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=mcl, partition_size=part,
+                           workspace=torch.empty(need, dtype=torch.uint8, device=pool.device))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)  # same kernels, same summation order: identical bits
+        want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+        err = float(np.abs(out.cpu().numpy().astype(np.float64) - want).max())
+        say(f"    bit-identical to pa_decode; max abs err vs oracle {err:.3e}")
+        assert err <= ATOL
+
+
+def test_noalloc_single_partition_and_empty_batch():
+    w = make_custom(name="noalloc-short", seed=97, dtype="bf16", num_blocks=40, num_q_heads=8, num_kv_heads=2,
+                    head_dim=64, block_size=16, lengths=[100, 5, 300])
+    st = w.steps[0]
+    pool = device_pool(w)
+    q, tables, lens = to_dev(st.q, w.dtype), i32(w.block_tables), i32(st.context_lens)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), device=pool.device)
+    assert noalloc(pool, q, tables, lens, w.scale, 300, 512, out) == 0
+    ref = pa.pa_decode(pool, q, tables, lens, scale=float(w.scale), max_context_len=300, partition_size=512)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert noalloc(pool, q[:0], tables[:0], lens[:0], w.scale, 300, 0, out[:0]) == 0
+
+
+def test_noalloc_refuses_partials_beyond_the_array():
+    # 512 sequences x 32 query heads x 20 partitions of (128 + 2) floats = 170 MB > 32 MiB:
+    # refused before anything is launched
+    dev = "cuda:0"
+    pool = pa.PagedKVPool.empty(64, 8, 16, 128, torch.bfloat16, device=dev)
+    S, Hq, mcl, part = 512, 32, 40960, 2048
+    q = torch.zeros((S, Hq, 128), dtype=torch.bfloat16, device=dev)
+    tables = torch.zeros((S, mcl // 16), dtype=torch.int32, device=dev)
+    lens = torch.ones(S, dtype=torch.int32, device=dev)
+    out = torch.zeros((S, Hq, 128), device=dev)
+    assert pa.pa_decode_workspace_size(pool, S, Hq, mcl, part) > 32 << 20
+    assert noalloc(pool, q, tables, lens, 0.088, mcl, part, out) == -3
+    torch.cuda.synchronize()
+    assert not out.any()
