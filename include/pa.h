@@ -206,8 +206,10 @@ int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t 
                                  int32_t max_context_len);
 
 /*
- * Device workspace bytes pa_decode needs for these arguments: 0 when every
- * sequence fits one partition (no workspace needed), or a negative
+ * Device workspace bytes pa_decode needs for these arguments (the
+ * split-context partials and, for skewed batches of many pairs, the work
+ * list): 0 when every sequence fits one partition (no workspace needed), or
+ * a negative
  * pa_status for arguments pa_decode would refuse (a bad pool, negative
  * sizes, num_q_heads not a multiple of num_kv_heads, a partition_size that
  * is not a multiple of max(block_size, 16) or exceeds 512 blocks).  The pool
@@ -241,7 +243,12 @@ int64_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t 
  *                  initialisation.
  * Calls sharing a workspace must not overlap in time (calls on one stream
  * never do).  A call launches one kernel, plus a small combine kernel when
- * some sequence spans more than one partition.  Query head hq reads KV head
+ * some sequence spans more than one partition.  Batches of 1,024 or more
+ * (sequence, KV head) pairs whose sequences may span several partitions
+ * (skewed lengths) first launch a one-workgroup prepass that lists the
+ * (pair, partition) items with work, longest first, in the workspace; the
+ * decode's resident workgroups then take items from that list (results are
+ * the same bits as without it).  Query head hq reads KV head
  * hq / (num_q_heads / num_kv_heads); the group size must be 1, 2, 4 or 8.
  * At most 65,535 sequences, and (num_seqs * num_kv_heads + 8) * partitions
  * below 2^31 (PA_ERR_UNSUPPORTED otherwise).

@@ -47,7 +47,11 @@
 //   device-wide fences.  The combination order depends only on logical
 //   positions, so results are identical under any physical placement.
 
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "pa_internal.h"
 
@@ -282,13 +286,17 @@ struct Cfg {
 // stage).  V keeps the vector layout with the token order matched: at load
 // step i row r holds token 4r + i, and takes head hh's probability and
 // rescale factor from lane hh of its row.
-template <typename T, int D, int B, int G, int CH, int W, bool NT, bool MQ>
+// LIST: the workgroups walk a work list (skewed batches) instead of taking one
+// (pair, partition) each from the grid; a separate instantiation, so the
+// grid kernels keep their register budget.
+template <typename T, int D, int B, int G, int CH, int W, bool NT, bool MQ, bool LIST>
 __global__ void __launch_bounds__(64 * W)
 decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_heads,
               const char *__restrict__ q, float *__restrict__ out, const int32_t *__restrict__ tables,
               int max_blocks_per_seq, const int32_t *__restrict__ context_lens, int num_q_heads,
               float scale_log2, int max_context_len, int part_blocks, int max_parts, int num_pairs,
-              float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+              float *__restrict__ ws_o, float *__restrict__ ws_ml, const int32_t *__restrict__ items,
+              const int32_t *__restrict__ n_items, int32_t *__restrict__ next_item) {
   using C = Cfg<T, D, B, G, CH>;
   constexpr int kWaves = W;  // wavefronts per workgroup
   constexpr int kThreads = 64 * W;
@@ -315,14 +323,13 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // among the working ones (measured: with the partition index fastest, an
   // even partition count crowded the work onto a fraction of the compute
   // units, up to 2.7x slower).
-  const int wg = blockIdx.x, xcd = wg % kXcds, j = wg / kXcds;
-  const int per_xcd = (num_pairs + kXcds - 1) / kXcds;
-  const int pair = (j % per_xcd) * kXcds + xcd, p = j / per_xcd;
-  if (pair >= num_pairs) return;
-  const int h = pair % num_kv_heads, s = pair / num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int row = lane >> 4, col = lane & 15;
+
+  // One (sequence-and-KV-head pair, partition) work item; a return ends the item.
+  auto run_item = [&](const int pair, const int p) __attribute__((always_inline)) {
+  const int h = pair % num_kv_heads, s = pair / num_kv_heads;
 
   // ---- loads that do not depend on the context length go out first, so
   // their latency overlaps that of the length itself: the queries (register
@@ -662,6 +669,105 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
       }
     }
   }
+  };
+
+  if constexpr (!LIST) {
+    // the grid holds one workgroup per (pair, partition)
+    const int wg = blockIdx.x, xcd = wg % kXcds, j = wg / kXcds;
+    const int per_xcd = (num_pairs + kXcds - 1) / kXcds;
+    const int pair = (j % per_xcd) * kXcds + xcd, p = j / per_xcd;
+    if (pair < num_pairs) run_item(pair, p);
+  } else {
+    // Work list (skewed batches of many pairs): the items with work, longest
+    // first.  A grid of resident workgroups takes item blockIdx.x first, then
+    // the next untaken one from a counter (grid + the counter's old value),
+    // fetched while the current item runs.  Every workgroup leaves the loop
+    // once the index passes the item count, which it reads once.
+    __shared__ int s_next_item;
+    const int n = __builtin_amdgcn_readfirstlane(*n_items);
+    int i = blockIdx.x;
+    while (i < n) {
+      int grabbed = 0;
+      if (tid == 0) grabbed = atomicAdd(next_item, 1);
+      const int it = __builtin_amdgcn_readfirstlane(items[i]);
+      const int pair = it / max_parts;
+      run_item(pair, it - pair * max_parts);
+      if (tid == 0) s_next_item = (int)gridDim.x + grabbed;
+      __syncthreads();
+      i = s_next_item;
+      __syncthreads();  // every thread has read it before thread 0 writes the next
+    }
+  }
+}
+
+// The work list of a decode call over a skewed batch: every (pair,
+// partition) item that has work -- one per partition a sequence spans, a
+// single one for an empty or invalid context (it writes that sequence's
+// zero or NaN rows) -- sorted longest first (a counting sort on the item's
+// length in 1/256ths of a partition), all KV heads of a (sequence,
+// partition) next to each other from a multiple of the head count.  One
+// workgroup; the order inside a length class follows atomics and does not
+// matter (every item writes its own outputs, and the partitions of a
+// sequence are combined in partition order).  Also resets the counter the
+// decode's workgroups take items from.
+constexpr int kListThreads = 1024;
+constexpr int kListBuckets = 256;
+
+__device__ __forceinline__ int item_bucket(int L, int np, int p, int part_tokens) {
+  if (np < 1) return 0;  // empty or invalid context: writes its rows only
+  const int len = min(part_tokens, L - p * part_tokens);
+  return (int)((int64_t)len * (kListBuckets - 1) / part_tokens);
+}
+
+__global__ void __launch_bounds__(kListThreads)
+worklist_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int num_kv_heads, int max_context_len,
+                int max_tokens_per_row, int part_tokens, int max_parts, int32_t *__restrict__ items,
+                int32_t *__restrict__ n_items, int32_t *__restrict__ next_item) {
+  __shared__ int s_count[kListBuckets];
+  __shared__ int s_next[kListBuckets];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kListBuckets; b += kListThreads) s_count[b] = 0;
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kListThreads) {
+    const int L = context_lens[s];
+    const int np = partitions_of(L, max_context_len, max_tokens_per_row, part_tokens);
+    for (int p = 0; p < max(np, 1); ++p) atomicAdd(&s_count[item_bucket(L, np, p, part_tokens)], 1);
+  }
+  __syncthreads();
+  // start of each length class, longest first: an exclusive scan of the
+  // classes in descending order, one class per thread of the first 4 waves
+  static_assert(kListBuckets == 4 * 64, "four waves scan the classes");
+  __shared__ int s_wave_sum[4];
+  int c = 0, incl = 0;
+  if (tid < kListBuckets) {
+    c = s_count[kListBuckets - 1 - tid] * num_kv_heads;
+    incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if ((tid & 63) >= off) incl += y;
+    }
+    if ((tid & 63) == 63) s_wave_sum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < kListBuckets) {
+    int before = 0;
+    for (int w = 0; w < (tid >> 6); ++w) before += s_wave_sum[w];
+    s_next[kListBuckets - 1 - tid] = before + incl - c;
+    if (tid == kListBuckets - 1) {
+      *n_items = before + incl;
+      *next_item = 0;
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kListThreads) {
+    const int L = context_lens[s];
+    const int np = partitions_of(L, max_context_len, max_tokens_per_row, part_tokens);
+    for (int p = 0; p < max(np, 1); ++p) {
+      const int at = atomicAdd(&s_next[item_bucket(L, np, p, part_tokens)], num_kv_heads);
+      for (int h = 0; h < num_kv_heads; ++h) items[at + h] = (s * num_kv_heads + h) * max_parts + p;
+    }
+  }
 }
 
 // Combine the partitions of one (sequence, query head): D threads, one per
@@ -722,10 +828,32 @@ constexpr bool matrix_core_scores(bool bf16, int group, int block_size) {
   return bf16 && group == 8 && block_size >= 16;
 }
 
+// Workgroups of `kernel` (with `threads` threads) resident on the whole
+// device at once: the grid of a work-list launch.
+int resident_workgroups(const void *kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void *, int>, int> cache;  // (kernel, device) -> workgroups
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int n = per_cu * cus / kXcds * kXcds;
+  cache[key] = n;
+  return n;
+}
+
 template <typename T, int D, int B, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   const int pairs = a.num_seqs * a.pool.num_kv_heads;
-  const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds) * kXcds * a.num_partitions);
+  const int64_t grid_items = (int64_t)((pairs + kXcds - 1) / kXcds) * kXcds * a.num_partitions;
   // Work shape per launch (measured on MI355X; see the partition choice):
   // - groups up to 4: 4-waves workgroups with 4-token stages (less in flight
   //   per wave; short contexts reach their first score sooner: up to 27 %
@@ -738,10 +866,15 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   //   (16-token stages); otherwise 8-token stages up to 2,048-token
   //   partitions, 16-token stages for the long partitions of a few long
   //   sequences.
+  const bool listed = a.items != nullptr;
   auto pick = [&](auto ch, auto w, auto mq) {
     constexpr int CH = decltype(ch)::value, W = decltype(w)::value;
     constexpr bool MQ = decltype(mq)::value;
-    return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true, MQ> : decode_kernel<T, D, B, G, CH, W, false, MQ>;
+    if (listed)
+      return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true, MQ, true>
+                            : decode_kernel<T, D, B, G, CH, W, false, MQ, true>;
+    return a.stream_loads ? decode_kernel<T, D, B, G, CH, W, true, MQ, false>
+                          : decode_kernel<T, D, B, G, CH, W, false, MQ, false>;
   };
   using vec = std::false_type;
   using ch4 = std::integral_constant<int, 4>;
@@ -761,11 +894,22 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
     kernel = pick(ch8{}, w8{}, vec{});
     waves = 8;
   }
-  hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream,
+  int64_t grid = grid_items;
+  if (a.items != nullptr) {
+    const int resident = resident_workgroups(reinterpret_cast<const void *>(kernel), 64 * waves);
+    if (resident <= 0) return hipErrorInvalidValue;
+    grid = std::min<int64_t>(grid_items, resident);
+    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kListThreads), 0, stream, a.context_lens, a.num_seqs,
+                       a.pool.num_kv_heads, a.max_context_len, a.max_blocks_per_seq * B, a.partition_blocks * B,
+                       a.num_partitions, a.items, a.n_items, a.next_item);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * waves), 0, stream,
                      static_cast<const char *>(a.pool.base), a.pool.num_blocks, a.pool.num_kv_heads,
                      static_cast<const char *>(a.q), a.out, a.block_tables, a.max_blocks_per_seq,
                      a.context_lens, a.num_q_heads, a.scale * kLog2e, a.max_context_len, a.partition_blocks,
-                     a.num_partitions, pairs, a.ws_o, a.ws_ml);
+                     a.num_partitions, pairs, a.ws_o, a.ws_ml, a.items, a.n_items, a.next_item);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a.ws_o, a.ws_ml,

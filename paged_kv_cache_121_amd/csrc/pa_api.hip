@@ -286,17 +286,27 @@ int prepare_decode(const pa_pool *pool, const void *q, float *out, const int32_t
   a->partition_blocks = part / d.block_size;
   a->num_partitions = parts;
   a->stream_loads = (flags & PA_DECODE_KEEP_CACHED) == 0;
-  if (parts > 1) *ws_need = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts).total;
+  *ws_need = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts,
+                                     decode_uses_work_list(num_seqs, d.num_kv_heads, parts))
+                  .total;
   return PA_OK;
 }
 
-// Points the split-context partials of `a` into a workspace of the size
-// prepare_decode asked for (256-byte aligned).
+// Points the split-context partials and the work list of `a` into a
+// workspace of the size prepare_decode asked for (256-byte aligned).
 void bind_workspace(DecodeArgs *a, char *base) {
-  const WorkspaceLayout w =
-      decode_workspace_layout(a->num_seqs, a->num_q_heads, a->pool.num_kv_heads, a->pool.head_dim, a->num_partitions);
-  a->ws_o = reinterpret_cast<float *>(base + w.o_off);
-  a->ws_ml = reinterpret_cast<float *>(base + w.ml_off);
+  const bool list = decode_uses_work_list(a->num_seqs, a->pool.num_kv_heads, a->num_partitions);
+  const WorkspaceLayout w = decode_workspace_layout(a->num_seqs, a->num_q_heads, a->pool.num_kv_heads,
+                                                    a->pool.head_dim, a->num_partitions, list);
+  if (a->num_partitions > 1) {
+    a->ws_o = reinterpret_cast<float *>(base + w.o_off);
+    a->ws_ml = reinterpret_cast<float *>(base + w.ml_off);
+  }
+  if (list) {
+    a->items = reinterpret_cast<int32_t *>(base + w.items_off);
+    a->n_items = reinterpret_cast<int32_t *>(base + w.n_items_off);
+    a->next_item = a->n_items + 1;
+  }
 }
 
 // ---- decode without allocation (pa_decode_noalloc): the split-context
@@ -345,14 +355,28 @@ int scratch_address(hipStream_t stream, char **out) {
 }  // namespace
 
 WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                        int num_partitions) {
+                                        int num_partitions, bool work_list) {
   WorkspaceLayout w{};
-  const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions;
-  w.o_off = 0;
-  w.ml_off = align_up(rows * head_dim * sizeof(float));
-  w.total = w.ml_off + align_up(rows * 2 * sizeof(float));
-  (void)num_kv_heads;
+  size_t off = 0;
+  if (num_partitions > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions;
+    w.o_off = off;
+    off += align_up(rows * head_dim * sizeof(float));
+    w.ml_off = off;
+    off += align_up(rows * 2 * sizeof(float));
+  }
+  if (work_list) {
+    w.items_off = off;
+    off += align_up((size_t)num_seqs * num_kv_heads * num_partitions * sizeof(int32_t));
+    w.n_items_off = off;
+    off += align_up(2 * sizeof(int32_t));
+  }
+  w.total = off;
   return w;
+}
+
+bool decode_uses_work_list(int num_seqs, int num_kv_heads, int num_partitions) {
+  return num_partitions > 1 && (int64_t)num_seqs * num_kv_heads >= kManyPairs;
 }
 
 }  // namespace pa
@@ -489,10 +513,11 @@ int64_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t 
   if (num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   const int part = resolve_partition(d, num_seqs, num_q_heads, max_context_len, partition_size);
   if (part < 0) return part;
-  if (num_seqs == 0 || max_context_len == 0) return 0;
-  const int parts = (max_context_len + part - 1) / part;
-  if (parts <= 1) return 0;
-  return (int64_t)decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts).total;
+  if (num_seqs == 0) return 0;
+  const int parts = max_context_len == 0 ? 1 : (max_context_len + part - 1) / part;  // as pa_decode
+  return (int64_t)decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts,
+                                          decode_uses_work_list(num_seqs, d.num_kv_heads, parts))
+      .total;
 }
 
 int pa_decode(const pa_pool *pool, const void *q, float *out, const int32_t *block_tables,
