@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the summary of workloads 3-5 in the decode line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill summary in the decode line")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="instead of the benchmark: HBM read rate of a 1 GiB buffer read in order and in "
+                         "randomly placed 4/16/64 KiB pieces (the decode kernel's practical ceiling)")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the read-ceiling summary in the decode line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="instead of the benchmark: run pa_block_copy over PAIRS distinct block pairs "
                          "(known bytes) 5 times, for scaling hardware byte counters")
@@ -208,41 +212,123 @@ def prefix_cache_timing(seed: int = 0):
             "decode_step_bookkeeping_us": round(float(np.median(t_step)) * 1e6, 1)}
 
 
-def cpu_baseline(w, n_seqs: int, got=None):
-    """The float64 oracle doing the step (cache write, then decode) for a bounded sample of
-    the same workload, one thread.  Each sampled sequence's blocks are gathered into a
-    private pool (the step's copy-on-write sources included), its new token written, and
-    all its query heads decoded.  With ``got`` (the GPU's output of the same step) the
-    sampled rows are compared."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import paged
+def _oracle_step_tasks(w, seqs):
+    """The oracle's inputs for the step of workload ``w`` on sequences ``seqs``: each
+    sequence's blocks as generated (the step's copy-on-write sources in place of their copies)
+    with its new token's write to replay (``oracle.parallel.sequence_task``)."""
+    from oracle.parallel import sequence_task
     st = w.steps[0]
-    B = w.block_size
     cow = dict(zip(st.cow_dst.tolist(), st.cow_src.tolist()))
+    tasks = []
+    for s in seqs:
+        L = int(st.context_lens[s])
+        row = np.array([cow.get(int(b), int(b)) for b in w.block_tables[s, :-(-L // w.block_size)]], dtype=np.int64)
+        mine = np.nonzero(st.write_seq == s)[0]
+        tasks.append(sequence_task(w.pool, row, L, st.q[s], float(w.scale),
+                                   (st.write_pos[mine], st.k_new[mine], st.v_new[mine])))
+    return tasks
+
+
+def cpu_baseline(w, n_seqs: int, got=None):
+    """The float64 oracle doing the step (cache write, then decode, every query head) on the
+    host's cores: (1) one thread on the first ``n_seqs`` sequences, (2) every sequence of the
+    step in a pool of worker processes, one BLAS thread each, on up to 16 of the cores this
+    process may use.  Each sequence's blocks are taken out of the generated pool (copy-on-write
+    sources included), its new token written, its query heads decoded.  With ``got`` (the GPU's
+    output of the same step) every computed row is compared."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle.parallel import host_cores, run_task, run_tasks, worker_pool
+    st = w.steps[0]
+    elt = w.elem_bytes
+    kv_of = [int(st.context_lens[s]) * 2 * w.num_kv_heads * w.head_dim * elt for s in range(w.num_seqs)]
+    blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")} for d in threadpool_info()]
+    err = 0.0
+    # (1) one thread
     sel = list(range(min(n_seqs, w.num_seqs)))
-    dt, kv, err = 0.0, 0, 0.0
+    tasks = _oracle_step_tasks(w, sel)
     with threadpool_limits(limits=1):
-        for s in sel:
-            L = int(st.context_lens[s])
-            rows = [int(b) for b in w.block_tables[s, :-(-L // B)]]
-            t0 = time.perf_counter()
-            small = np.stack([w.pool[cow.get(b, b)] for b in rows])
-            tbl = np.arange(len(rows), dtype=np.int32)[None, :]
-            mine = np.nonzero(st.write_seq == s)[0]
-            slot = paged.slot_mapping_ref(tbl, np.zeros(len(mine), dtype=np.int32), st.write_pos[mine], B)
-            small = paged.cache_write_ref(small, st.k_new[mine], st.v_new[mine], slot)
-            want = paged.decode_ref(small, st.q[s:s + 1], tbl, [L], float(w.scale))
-            dt += time.perf_counter() - t0
-            kv += L * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
-            if got is not None:
-                err = max(err, float(np.abs(got[s].astype(np.float64) - want[0]).max()))
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle step (cache write + decode, all {w.num_q_heads} query heads) of "
-                      f"sequences 0-{len(sel) - 1} of the same workload: {kv / 1e9:.3f} GB of KV in "
-                      f"{dt:.1f} s, one thread",
-            "seq_layers_per_s": len(sel) / dt,
+        t0 = time.perf_counter()
+        res1 = [run_task(t) for t in tasks]
+        dt1 = time.perf_counter() - t0
+    kv1 = sum(kv_of[s] for s in sel)
+    # (2) every sequence, all cores (pool started before the clock: process start-up is not oracle work)
+    cores = host_cores()
+    workers = min(cores, 16)
+    tasks = _oracle_step_tasks(w, range(w.num_seqs))
+    with worker_pool(workers) as ex:
+        run_tasks(tasks[:workers], pool=ex)  # every worker up and its imports done
+        t0 = time.perf_counter()
+        res = run_tasks(tasks, pool=ex)
+        dtn = time.perf_counter() - t0
+    kvn = sum(kv_of)
+    if got is not None:
+        for s, want in enumerate(res):
+            err = max(err, float(np.abs(got[s].astype(np.float64) - want).max()))
+        for s, want in zip(sel, res1):
+            assert np.array_equal(want, res[s])
+    return {"value": kvn / dtn / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 oracle step (cache write + decode, all {w.num_q_heads} query heads) of all "
+                      f"{w.num_seqs} sequences of the same workload ({kvn / 1e9:.3f} GB of KV) in {dtn:.1f} s on "
+                      f"{workers} worker processes, one BLAS thread each",
+            "host_cores_available": cores, "blas_threads_main_process": blas,
+            "seq_layers_per_s": w.num_seqs / dtn,
+            "single_thread": {"value": kv1 / dt1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": f"sequences 0-{len(sel) - 1}: {kv1 / 1e9:.3f} GB of KV in {dt1:.1f} s",
+                              "seq_layers_per_s": len(sel) / dt1},
+            "rows_compared": w.num_seqs * w.num_q_heads if got is not None else 0,
             "max_abs_err_vs_gpu": err if got is not None else None}
+
+
+def read_ceiling(dev, total_bytes: int = 1 << 30, reps: int = 20, seed: int = 0):
+    """HBM read rate of a ``total_bytes`` buffer read once, in order and in randomly placed
+    pieces of 4, 16 and 64 KiB (read_probe.hip: the decode kernel's 16-byte non-temporal loads,
+    1 KiB per wavefront load), best over a sweep of grid sizes and loads in flight.  The decode
+    of a paged cache reads 4 KiB (block, head) tiles of randomly placed blocks, so the random
+    4 KiB rate is its practical ceiling; HIP events over ``reps`` launches after a settle."""
+    import ctypes
+
+    import torch
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (python -m paged_kv_cache_121_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.pa_probe_read.restype = ctypes.c_int
+    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.empty(total_bytes, dtype=torch.uint8, device=dev)
+    grids, unrolls = (512, 1024, 2048, 4096), (1, 2, 4, 8)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator().manual_seed(seed)
+    out = {}
+    for label, piece, shuffled in (("in_order", 65536, False), ("random_4KiB", 4096, True),
+                                   ("random_16KiB", 16384, True), ("random_64KiB", 65536, True)):
+        n = total_bytes // piece
+        order = (torch.randperm(n, generator=g) if shuffled else torch.arange(n)).to(torch.int32).to(dev)
+        rates = {}
+        for grid in grids:
+            for u in unrolls:
+                def run():
+                    rc = lib.pa_probe_read(ctypes.c_void_p(buf.data_ptr()), piece, ctypes.c_void_p(order.data_ptr()),
+                                           n, grid, u, ctypes.c_void_p(sink.data_ptr()),
+                                           ctypes.c_void_p(stream.cuda_stream))
+                    assert rc == 0, rc
+                settle(run, ms=20.0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                rates[f"grid{grid}_x{u}"] = total_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        best = max(rates, key=rates.get)
+        out[label] = {"piece_bytes": piece, "best_gbs": round(rates[best], 1),
+                      "pct_hbm_peak": round(100 * rates[best] / HBM_PEAK_GBS, 2), "best_launch": best,
+                      "all_gbs": {k: round(v, 1) for k, v in rates.items()}}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"bytes": total_bytes, "reps": reps, **out}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -436,6 +522,23 @@ def d2d_copy_gbs(dev, nbytes: int = 2 << 30, reps: int = 10):
     return {"bytes": nbytes, "read_gbs": round(nbytes / t / 1e9, 1), "read_plus_write_gbs": round(2 * nbytes / t / 1e9, 1)}
 
 
+def unique_kv_bytes(w, k: int) -> int:
+    """K/V bytes of the distinct physical slots step k's decode reads: a block shared by
+    several sequences (a common prefix) counts once, with the most tokens any of its readers
+    uses (a sequence uses a block's slots from offset 0).  Equal to the logical bytes when no
+    block is shared."""
+    st = w.steps[k]
+    B = w.block_size
+    used = {}
+    for s in range(w.num_seqs):
+        L = int(st.context_lens[s])
+        nb = -(-L // B)
+        for j, b in enumerate(w.block_tables[s, :nb].tolist()):
+            n = B if j < nb - 1 else L - (nb - 1) * B
+            used[b] = max(used.get(b, 0), n)
+    return sum(used.values()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+
+
 def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
     """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping and cache write
     in one launch, decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak.
@@ -463,6 +566,7 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
 
         pool = pa.PagedKVPool(d(w.pool))
         del w.pool
+        unique_kv = unique_kv_bytes(w, 0)
         tables = i32(w.block_tables)
         keep = bool(w.meta.get("prefix_tokens"))
         steps = []
@@ -514,6 +618,9 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
                                "decode_gbs": round(kv / ms / 1e6, 1),
                                "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
                                "kv_cache_policy": "keep cached" if keep else "stream",
+                               "unique_kv_bytes": unique_kv,
+                               "decode_gbs_unique": round(unique_kv / ms / 1e6, 1),
+                               "pct_hbm_peak_unique": round(100 * unique_kv / ms / 1e6 / HBM_PEAK_GBS, 2),
                                "partition_size": pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads,
                                                                              steps[0][8])}
         print(f"[bench] workload {k}: decode {out[f'workload{k}']['decode_us']} us "
@@ -627,6 +734,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, dev)
         return
+    if args.read_ceiling:
+        r = read_ceiling(dev)
+        print(json.dumps({"metric": "HBM read GB/s by access pattern (decode roofline reference)", "unit": "GB/s",
+                          "n_gpus": 1, "higher_is_better": True, "data": "1 GiB device buffer", **r}), flush=True)
+        return
     if args.swap:
         r = swap_measurement(dev)
         print(json.dumps({"metric": "swap copy GB/s (device <-> pinned host)", "unit": "GB/s", "n_gpus": 1,
@@ -738,6 +850,7 @@ def main():
             sys.exit(1)
     host_bm = block_manager_timing(w)
     d2d = d2d_copy_gbs(dev)
+    ceiling = None if args.no_read_ceiling else read_ceiling(dev)
     others = None if args.no_other_workloads else other_workloads(dev)
     host_prefix = prefix_cache_timing()
     prefill = None
@@ -782,6 +895,7 @@ def main():
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
         "d2d_copy": d2d,
+        "read_ceiling": ceiling,
         "other_workloads": others,
         "block_manager": host_bm,
         "prefix_cache": host_prefix,

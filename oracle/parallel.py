@@ -52,13 +52,20 @@ def run_task(task) -> np.ndarray:
     return paged.decode_ref(blocks, q_row[None], table, [length], scale)[0]
 
 
+def _one_blas_thread() -> None:
+    """Worker start-up: one BLAS thread per process (the workers already use every core)."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
 def worker_pool(workers: int | None = None) -> concurrent.futures.ProcessPoolExecutor:
     """A pool of ``workers`` spawned processes (default: every core this process may use, at
-    most 16), to pass to several ``run_tasks`` calls."""
+    most 16), one BLAS thread each, to pass to several ``run_tasks`` calls."""
     if workers is None:
         workers = min(host_cores(), 16)
     return concurrent.futures.ProcessPoolExecutor(max_workers=max(1, workers),
-                                                  mp_context=multiprocessing.get_context("spawn"))
+                                                  mp_context=multiprocessing.get_context("spawn"),
+                                                  initializer=_one_blas_thread)
 
 
 def run_tasks(tasks, pool: concurrent.futures.Executor | None = None, workers: int | None = None,

@@ -4,7 +4,9 @@
 
 Every HIP translation unit under csrc/ is compiled to an object in
 ``_build/`` (in parallel), then linked into ``paged_kv_cache_121_amd/libpa.so``.
-All device code is compiled with packed-fp32 instructions disabled.
+The benchmark's HBM read-rate probe (``read_probe.hip`` beside bench.py) is
+built into ``libpa_probe.so`` next to it, apart from the library.  All device
+code is compiled with packed-fp32 instructions disabled.
 """
 
 from __future__ import annotations
@@ -21,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+PROBE_SRC = os.path.join(ROOT, "read_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libpa_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]  # HIP: device and host code
@@ -76,7 +80,21 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(hipcc, extra, verbose)
     return LIB
+
+
+def build_probe(hipcc: str, extra: list[str], verbose: bool = False) -> str:
+    """libpa_probe.so: the benchmark's HBM read-rate probe."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, *COMMON_FLAGS, *extra, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for read_probe.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
