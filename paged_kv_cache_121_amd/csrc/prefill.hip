@@ -359,20 +359,23 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) v_base[nt] = v_lds8<D>(4 * grp + r16 / 4, 4 * nt + (r16 & 3));
 
-  // S^T of tile t: sacc[rg][kt] = K[16kt .. +16] Q_rg^T (raw, unscaled); each K operand serves every row group
+  // S^T of tile t: sacc[rg][kt] = K[16kt .. +16] Q_rg^T (raw, unscaled); each K operand serves every row group.
+  // The 32-dim steps run outermost, so the MFMAs that accumulate into one
+  // score tile are 8 apart (measured 0.5 % faster than tile by tile).
   auto qk = [&](const char *kt_lds, f32x4_t (&sacc)[kRG][4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) sacc[rg][kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
+    for (int kc = 0; kc < C::KC; ++kc)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           sacc[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
       }
-    }
   };
   // Softmax, first half: mask tile t's raw scores in place (diagonal tiles
   // only), take each row's maximum and raise the running maximum, rescaling
@@ -458,10 +461,10 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     // the schedule is pinned to (2 reads of a later step, 4 MFMAs of this one)
     // so the reads' latency overlaps the matrix work (left to itself the
     // scheduler waits on each step's reads just before its MFMAs).
-    constexpr int NS = 2 * C::NT;  // (nt, ks) steps
+    constexpr int NS = 2 * C::NT;  // (nt, ks) steps, ks outermost: consecutive steps feed different output tiles
     bf16x8_t vq[kVAhead];
     auto rdv = [&](int st) __attribute__((always_inline)) {
-      const int nt = st / 2, ks = st % 2;
+      const int nt = st % C::NT, ks = st / C::NT;
       const i16x4_t lo4 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + v_base[nt] + 32 * ks * C::ROWB));
       const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -473,7 +476,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const int nt = st / 2, ks = st % 2;
+      const int nt = st % C::NT, ks = st / C::NT;
       const bf16x8_t vb = vq[st % kVAhead];
       if (st + kVAhead < NS) vq[st % kVAhead] = rdv(st + kVAhead);
 #pragma unroll
