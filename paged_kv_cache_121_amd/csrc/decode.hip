@@ -728,10 +728,13 @@ worklist_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int num_
   const int tid = threadIdx.x;
   for (int b = tid; b < kListBuckets; b += kListThreads) s_count[b] = 0;
   __syncthreads();
+  // a sequence's partitions before its last are full (the longest class), so
+  // each sequence takes at most two atomics per pass
   for (int s = tid; s < num_seqs; s += kListThreads) {
     const int L = context_lens[s];
     const int np = partitions_of(L, max_context_len, max_tokens_per_row, part_tokens);
-    for (int p = 0; p < max(np, 1); ++p) atomicAdd(&s_count[item_bucket(L, np, p, part_tokens)], 1);
+    if (np > 1) atomicAdd(&s_count[kListBuckets - 1], np - 1);
+    atomicAdd(&s_count[item_bucket(L, np, max(np, 1) - 1, part_tokens)], 1);
   }
   __syncthreads();
   // start of each length class, longest first: an exclusive scan of the
@@ -763,10 +766,15 @@ worklist_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int num_
   for (int s = tid; s < num_seqs; s += kListThreads) {
     const int L = context_lens[s];
     const int np = partitions_of(L, max_context_len, max_tokens_per_row, part_tokens);
-    for (int p = 0; p < max(np, 1); ++p) {
-      const int at = atomicAdd(&s_next[item_bucket(L, np, p, part_tokens)], num_kv_heads);
-      for (int h = 0; h < num_kv_heads; ++h) items[at + h] = (s * num_kv_heads + h) * max_parts + p;
+    const int last = max(np, 1) - 1;
+    if (np > 1) {
+      const int at = atomicAdd(&s_next[kListBuckets - 1], (np - 1) * num_kv_heads);
+      for (int p = 0; p < last; ++p)
+        for (int h = 0; h < num_kv_heads; ++h)
+          items[at + p * num_kv_heads + h] = (s * num_kv_heads + h) * max_parts + p;
     }
+    const int at = atomicAdd(&s_next[item_bucket(L, np, last, part_tokens)], num_kv_heads);
+    for (int h = 0; h < num_kv_heads; ++h) items[at + h] = (s * num_kv_heads + h) * max_parts + last;
   }
 }
 
