@@ -539,9 +539,11 @@ def unique_kv_bytes(w, k: int) -> int:
     return sum(used.values()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
 
 
-def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
+def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20, check: bool = True):
     """Every step of workloads 3-5 in turn (copy-on-write copies, slot mapping and cache write
     in one launch, decode) and decode alone on step 0: HIP-event times, KV GB/s and % of peak.
+    With ``check``, step 0's output (every row) is compared with the float64 oracle run on
+    up to 16 worker processes, whose time is reported beside it.
     Output and workspace are allocated once, and the decode-only launches run back to back
     between one pair of events (a call of 30 us is otherwise timed with the binding's per-call
     host work in it).  "4tp8" is one GPU's share of workload 4 under 8-way tensor parallelism
@@ -565,7 +567,6 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
             return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
         pool = pa.PagedKVPool(d(w.pool))
-        del w.pool
         unique_kv = unique_kv_bytes(w, 0)
         tables = i32(w.block_tables)
         keep = bool(w.meta.get("prefix_tokens"))
@@ -610,6 +611,26 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         kv = w.kv_bytes(0)
+        # step 0's output again (later steps write only positions step 0 does not read), against
+        # the oracle on every sequence
+        oracle = None
+        if check:
+            from oracle.parallel import host_cores, run_tasks, worker_pool
+            got0 = run(0, True).cpu().numpy()
+            workers = min(host_cores(), 16)
+            tasks = _oracle_step_tasks(w, range(w.num_seqs))
+            with worker_pool(workers) as ex:
+                t1 = time.perf_counter()
+                want = run_tasks(tasks, pool=ex)
+                t_or = time.perf_counter() - t1
+            err = max(float(np.abs(got0[s].astype(np.float64) - wv).max()) for s, wv in enumerate(want))
+            if not err <= 2e-3:
+                print(f"[bench] PARITY FAILURE in workload {k}: max abs err {err}", file=sys.stderr)
+                sys.exit(1)
+            oracle = {"rows": w.num_seqs * w.num_q_heads, "max_abs_err": err, "oracle_s": round(t_or, 2),
+                      "cores": workers, "kind": "float64 oracle, step 0, every sequence (worker start-up excluded)"}
+            del tasks, want
+        del w.pool
         name = (CONFIG_NAMES[4] + "; one GPU's share at 8-way tensor parallelism: 1 KV head, 8 query heads"
                 if k == "4tp8" else CONFIG_NAMES[k])
         out[f"workload{k}"] = {"workload": name, "steps": len(steps), "timed_steps": len(order),
@@ -622,7 +643,8 @@ def other_workloads(dev, ks=(3, 4, 5, "4tp8"), reps: int = 20):
                                "decode_gbs_unique": round(unique_kv / ms / 1e6, 1),
                                "pct_hbm_peak_unique": round(100 * unique_kv / ms / 1e6 / HBM_PEAK_GBS, 2),
                                "partition_size": pa.pa_decode_partition_size(pool, w.num_seqs, w.num_q_heads,
-                                                                             steps[0][8])}
+                                                                             steps[0][8]),
+                               "oracle_check": oracle}
         print(f"[bench] workload {k}: decode {out[f'workload{k}']['decode_us']} us "
               f"({out[f'workload{k}']['pct_hbm_peak']} %), step {out[f'workload{k}']['step_us']} us, "
               f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -851,7 +873,7 @@ def main():
     host_bm = block_manager_timing(w)
     d2d = d2d_copy_gbs(dev)
     ceiling = None if args.no_read_ceiling else read_ceiling(dev)
-    others = None if args.no_other_workloads else other_workloads(dev)
+    others = None if args.no_other_workloads else other_workloads(dev, check=not args.no_cpu_baseline)
     host_prefix = prefix_cache_timing()
     prefill = None
     if not args.no_prefill:

@@ -8,10 +8,14 @@ float32 values, or bf16 bit patterns as uint16.  Blocks that hold no token of
 any sequence are filled with NaN so that a kernel reading outside a
 sequence's blocks cannot go unnoticed.
 
-Seeds: workload ``k`` draws from ``numpy.random.default_rng(k)`` (reduced
-variants from ``default_rng(100 + k)``), in this order: lengths, block
-placement, resident K/V contents, then per step the query and the new
-tokens' K and V.
+Seeds (reduced variants use ``100 + k`` in place of ``k``): workloads 2 and
+3 draw their lengths from ``numpy.random.default_rng(k)`` and everything
+else -- block placement, resident K/V contents, then per step the query and
+the new tokens' K and V, in that order -- from ``default_rng(k + 1000)``;
+workload 5 draws its lengths from ``default_rng(5)`` (or the next seed that
+fits the pool) and the rest from that seed plus 1000; workloads 1 and 4
+draw placement, contents and steps from ``default_rng(k)``.  The
+tensor-parallel share of workload 4 uses ``default_rng(4 + 1000 * tp)``.
 """
 
 from __future__ import annotations
