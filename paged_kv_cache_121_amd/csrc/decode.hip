@@ -315,14 +315,14 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   __shared__ float s_l[kWaves][G];
   __shared__ int s_bad[kWaves];
 
-  // One-dimensional grid.  Workgroup wg runs on XCD wg % kXcds; XCD x takes
-  // the (sequence, KV head) pairs x, x + kXcds, ..., first partition 0 of
-  // each, then partition 1 of each, and so on.  In a batch of mixed lengths
-  // most pairs have one partition, so the workgroups that exit at once all
-  // sit at the end of the dispatch order instead of in a regular pattern
-  // among the working ones (measured: with the partition index fastest, an
-  // even partition count crowded the work onto a fraction of the compute
-  // units, up to 2.7x slower).
+  // One-dimensional grid (see the dispatch at the end).  Workgroup wg runs on
+  // XCD wg % kXcds; each XCD takes an equal share of the (sequence, KV head)
+  // pairs, first partition 0 of each, then partition 1 of each, and so on.
+  // In a batch of mixed lengths most pairs have one partition, so the
+  // workgroups that exit at once all sit at the end of the dispatch order
+  // instead of in a regular pattern among the working ones (measured: with
+  // the partition index fastest, an even partition count crowded the work
+  // onto a fraction of the compute units, up to 2.7x slower).
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int row = lane >> 4, col = lane & 15;
@@ -672,10 +672,21 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   };
 
   if constexpr (!LIST) {
-    // the grid holds one workgroup per (pair, partition)
+    // The grid holds one workgroup per (pair, partition).  Streaming loads
+    // (no shared blocks), vector scores: XCD x takes the x-th eighth of the
+    // pairs in order, so the KV heads of a sequence -- the 4 KiB tiles that
+    // make up each of its 64 KiB blocks -- are read together by one XCD (1 %
+    // faster than head by head on the Qwen3-8B batch-64 layer).  Otherwise
+    // XCD x takes pairs x, x + 8, ..., i.e. KV head x of every sequence at 8
+    // KV heads: with blocks shared by several sequences (cached loads) the
+    // sharers of a block then read it through one L2 (4 % faster than by
+    // sequence on a shared prefix), and the matrix-core kernel's few long
+    // partitions measured no better by sequence.
+    constexpr bool kBySequence = NT && !MQ;
     const int wg = blockIdx.x, xcd = wg % kXcds, j = wg / kXcds;
     const int per_xcd = (num_pairs + kXcds - 1) / kXcds;
-    const int pair = (j % per_xcd) * kXcds + xcd, p = j / per_xcd;
+    const int pair = kBySequence ? xcd * per_xcd + (j % per_xcd) : (j % per_xcd) * kXcds + xcd;
+    const int p = j / per_xcd;
     if (pair < num_pairs) run_item(pair, p);
   } else {
     // Work list (skewed batches of many pairs): the items with work, longest
@@ -778,11 +789,15 @@ worklist_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int num_
   }
 }
 
-// Combine the partitions of one (sequence, query head): D threads, one per
-// output element.  The maximum over partitions is taken in parallel (thread d
-// reads partitions d, d + D, ...; then a workgroup reduction); the weighted
-// sums run in partition order with the loads of 8 partitions issued together,
-// so the result depends only on logical positions.
+// Combine the partitions of (sequence, query head) rows.  Both forms take
+// the maximum over partitions, then the weighted sums in partition order with
+// the loads of 8 partitions issued together, so the result depends only on
+// logical positions and is the same bits in both; rows of sequences that fit
+// one partition were written by the decode itself and are skipped.
+//
+// combine_kernel: one workgroup of D threads per row, thread d holding dim d
+// (the maximum: thread d reads partitions d, d + D, ..., then a workgroup
+// reduction).  For calls with few rows, each spread over its own compute unit.
 template <int D>
 __global__ void __launch_bounds__(D)
 combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
@@ -793,7 +808,7 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
   __shared__ float s_max[kCombineWaves];
   const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int np = partitions_of(context_lens[s], max_context_len, max_tokens_per_row, part_tokens);
-  if (np <= 1) return;  // written by the decode kernel itself
+  if (np <= 1) return;
   const int64_t row = (int64_t)s * num_q_heads + hq;
   const float *ml = ws_ml + row * max_parts * 2;
   const float *o = ws_o + row * max_parts * D + d;
@@ -829,6 +844,66 @@ combine_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, 
     den += a * ml[2 * p + 1];
   }
   out[row * D + d] = num / den;
+}
+
+// combine_many_kernel: one wave per row, four rows per workgroup, lane l
+// holding dims DPL*l .. DPL*l + DPL-1 (the maximum: lane l reads partitions
+// l, l + 64, ..., then a wave reduction).  For calls with many rows, most of
+// which (in a skewed batch) need no combining: 4x fewer workgroups to
+// dispatch than one per row (1 % of a call over 512 x 32 rows; with few rows
+// it is 2-3 % slower than combine_kernel).
+constexpr int kCombineRows = 4;
+constexpr int64_t kCombineManyRows = 4096;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kCombineRows)
+combine_many_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
+                    const int32_t *__restrict__ context_lens, int num_seqs, int num_q_heads, int max_context_len,
+                    int max_tokens_per_row, int part_tokens, int max_parts) {
+  constexpr int DPL = D / 64;
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+  if (row >= (int64_t)num_seqs * num_q_heads) return;
+  const int s = (int)(row / num_q_heads);
+  const int np = partitions_of(context_lens[s], max_context_len, max_tokens_per_row, part_tokens);
+  if (np <= 1) return;
+  const float *ml = ws_ml + row * max_parts * 2;
+  const float *o = ws_o + row * max_parts * D + lane * DPL;
+  float M = kNegInf;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Ms = M == kNegInf ? 0.0f : M;
+  float num[DPL], den = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) num[e] = 0.0f;
+  int p = 0;
+  for (; p + kBatch <= np; p += kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch][DPL];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      mv[k] = ml[2 * (p + k)];
+      lv[k] = ml[2 * (p + k) + 1];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[k][e] = o[(int64_t)(p + k) * D + e];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float a = fast_exp2(mv[k] - Ms);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) num[e] += a * ov[k][e];
+      den += a * lv[k];
+    }
+  }
+  for (; p < np; ++p) {
+    const float a = fast_exp2(ml[2 * p] - Ms);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) num[e] += a * o[(int64_t)p * D + e];
+    den += a * ml[2 * p + 1];
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) out[row * D + lane * DPL + e] = num[e] / den;
 }
 
 // The one rule for which launches take their scores from the matrix cores.
@@ -920,9 +995,16 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
                      a.num_partitions, pairs, a.ws_o, a.ws_ml, a.items, a.n_items, a.next_item);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a.ws_o, a.ws_ml,
-                     a.out, a.context_lens, a.num_q_heads, a.max_context_len, a.max_blocks_per_seq * B,
-                     a.partition_blocks * B, a.num_partitions);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+  if (rows >= kCombineManyRows)
+    hipLaunchKernelGGL((combine_many_kernel<D>), dim3((unsigned)((rows + kCombineRows - 1) / kCombineRows)),
+                       dim3(64 * kCombineRows), 0, stream, a.ws_o, a.ws_ml, a.out, a.context_lens, a.num_seqs,
+                       a.num_q_heads, a.max_context_len, a.max_blocks_per_seq * B, a.partition_blocks * B,
+                       a.num_partitions);
+  else
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a.ws_o, a.ws_ml,
+                       a.out, a.context_lens, a.num_q_heads, a.max_context_len, a.max_blocks_per_seq * B,
+                       a.partition_blocks * B, a.num_partitions);
   return hipGetLastError();
 }
 
