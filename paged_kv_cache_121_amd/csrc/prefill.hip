@@ -16,7 +16,9 @@
 // reads the same K/V, and each K/V tile is loaded once for 8 waves (one
 // workgroup per CU at two waves per SIMD).  K/V tiles of 64 keys go from HBM
 // straight into LDS (global_load_lds_dwordx4, no registers on the way),
-// double-buffered, and each wave computes flash-attention style on its rows:
+// double-buffered, and each wave computes flash-attention style on its rows,
+// its matrix-core work and its softmax in alternate half-phases, out of step
+// with the other wave of its SIMD (the ping-pong at the tile loop):
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; A = K rows from LDS (ds_read_b128,
 //                 XOR-swizzled rows so 16 rows hit 16 different bank groups),
 //                 B = Q^T held in registers.  The C layout of S^T gives every
@@ -406,8 +408,11 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       mnew[rg] = __builtin_elementwise_maximum(m[rg], mt);
       upd[rg] = mnew[rg] > m[rg] + kPfRescaleThreshold;
     }
-    // one wave-uniform branch for both row groups (rare)
-    if (__builtin_amdgcn_ballot_w64(upd[0] || (kRG > 1 && upd[kRG - 1])) != 0) {
+    // one wave-uniform branch for all row groups (rare)
+    bool any_upd = false;
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) any_upd = any_upd || upd[rg];
+    if (__builtin_amdgcn_ballot_w64(any_upd) != 0) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
         const float alpha = upd[rg] ? pf_exp2(m[rg] - mnew[rg]) : 1.0f;
@@ -425,11 +430,11 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
     }
   };
-  // Softmax, second half, and O += P V(t): P = exp2(cs * s - m) in fp32 (the
-  // permuted key order), split into bf16 parts P_hi + P_lo; row sums P 1 and
-  // the V products on the bf16 matrix cores, each part in turn.
-  auto exp_pv = [&](const f32x4_t (&sacc)[kRG][4], const char *vt_lds) __attribute__((always_inline)) {
-    bf16x8_t ph[kRG][2], pl[kRG][2];
+  // Softmax, second half: P = exp2(cs * s - m) in fp32 (the permuted key
+  // order), split into bf16 parts P_hi + P_lo (P_hi the truncation, P_lo the
+  // rounded remainder); the row sums P 1 on the matrix cores, part by part.
+  auto make_p = [&](const f32x4_t (&sacc)[kRG][4], bf16x8_t (&ph)[kRG][2], bf16x8_t (&pl)[kRG][2])
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       const float nms = m[rg] == kPfNegInf ? 0.0f : -m[rg];
@@ -457,9 +462,13 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], ones, osum[rg], 0, 0, 0);
       }
     }
+  };
+  // O += P V: P_hi then P_lo against each V operand.
+  auto pv = [&](const bf16x8_t (&ph)[kRG][2], const bf16x8_t (&pl)[kRG][2], const char *vt_lds)
+                __attribute__((always_inline)) {
     // V operands are read kVAhead steps before the MFMAs that use them, and
-    // the schedule is pinned to (2 reads of a later step, 4 MFMAs of this one)
-    // so the reads' latency overlaps the matrix work (left to itself the
+    // the schedule is pinned to (4 reads of later steps, 8 MFMAs of this step
+    // pair) so the reads' latency overlaps the matrix work (left to itself the
     // scheduler waits on each step's reads just before its MFMAs).
     constexpr int NS = 2 * C::NT;  // (nt, ks) steps, ks outermost: consecutive steps feed different output tiles
     bf16x8_t vq[kVAhead];
@@ -473,86 +482,101 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     };
 #pragma unroll
     for (int st = 0; st < kVAhead; ++st) vq[st] = rdv(st);
-    __builtin_amdgcn_s_setprio(1);
+    // Steps go in pairs (output tiles nt, nt+1 of one key half): the P_hi
+    // and P_lo products into one tile are 2 kRG MFMAs apart.
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NS; st += 2) {
       const int nt = st % C::NT, ks = st / C::NT;
-      const bf16x8_t vb = vq[st % kVAhead];
+      const bf16x8_t vb0 = vq[st % kVAhead], vb1 = vq[(st + 1) % kVAhead];
       if (st + kVAhead < NS) vq[st % kVAhead] = rdv(st + kVAhead);
+      if (st + 1 + kVAhead < NS) vq[(st + 1) % kVAhead] = rdv(st + 1 + kVAhead);
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg)
-        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb, o[rg][nt], 0, 0, 0);
+        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb0, o[rg][nt], 0, 0, 0);
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg)
-        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb, o[rg][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRG, 0);  // MFMAs
+        o[rg][nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], vb1, o[rg][nt + 1], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg)
+        o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb0, o[rg][nt], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg)
+        o[rg][nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], vb1, o[rg][nt + 1], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kRG, 0);  // MFMAs
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
-  using buf0 = std::integral_constant<int, 0>;
-  using buf1 = std::integral_constant<int, 1>;
-  // ---- double buffering.  Iteration t: S(t), softmax(t) and PV(t) from
-  // buffers t%2; wait for tile t+1's loads (and zero its V rows past the
-  // context); barrier; start K(t+2) and V(t+2) into buffers t%2.
-  int ids[NBT];
-  fetch_ids(0, ids);
-  load_lds(0, ids, 0, false, s_k[0]);
-  load_lds(0, ids, kv_half, true, s_v[0]);
+  // ---- ping-pong.  Waves w and w + 4 share a SIMD (a workgroup's waves go
+  // to its CU's four SIMDs in turn).  Each wave alternates a matrix-core half
+  // (scores of tile t, P.V of tile t-1) and a vector half (row maxima and
+  // probabilities of tile t); waves 4-7 run one half-phase behind waves 0-3,
+  // so while one wave of a SIMD feeds the matrix cores the other runs its
+  // softmax, instead of both meeting in the same phase.  The matrix-core
+  // halves run at raised wave priority, so the arbiter gives an MFMA the issue
+  // slot before the other wave's vector instruction (2 % measured).  Every
+  // half-phase ends in a barrier.  Half-phase
+  // h = 2u (even) starts the loads of K(u+1) (buffer (u+1) % 2) and V(u)
+  // (buffer u % 2); half-phase 2u+1 waits for them before its barrier.  Wave
+  // group 0 runs M(u) in half-phase 2u and V(u) in 2u+1; group 1 runs M(u)
+  // in 2u+1 and V(u) in 2u+2.  K(u) and V(u-1) are read in M(u) only, so
+  // their buffers are free after half-phase 2u+1.
+  const int n_compute = min(ntiles, w_last_tile + 1);  // tiles with work for this wave (uniform)
+  const int grp1 = wave >= kPfWaves / 2;
+  int ids_k[NBT], ids_v[NBT];
+  fetch_ids(0, ids_v);
+  load_lds(0, ids_v, 0, false, s_k[0]);
+  if (ntiles > 1) fetch_ids(1, ids_k);
   wait_lds_loads();
-  zero_v_tail(s_v[0], 0);
   __syncthreads();
-  if (ntiles > 1) {
-    fetch_ids(1, ids);
-    load_lds(1, ids, 0, false, s_k[1]);
-    load_lds(1, ids, kv_half, true, s_v[1]);
-  }
   f32x4_t sc[kRG][4];
-  // one tile step; the arithmetic is skipped (COMPUTE false) for tiles past
-  // every row of this wave, which still take part in the loads and barriers
-  auto step = [&](int t, auto bt, auto compute) __attribute__((always_inline)) {
-    constexpr int b = decltype(bt)::value;
-    if (t + 2 < ntiles) fetch_ids(t + 2, ids);  // their latency hides behind this tile's work
-    if constexpr (decltype(compute)::value) {
-      // The MFMA phases run at raised wave priority, so the arbiter keeps
-      // feeding the matrix pipe while the other wave of the SIMD is in its
-      // softmax (1-2 % measured).
-      __builtin_amdgcn_s_setprio(1);
-      qk(s_k[b], sc);
-      __builtin_amdgcn_s_setprio(0);
+  bf16x8_t ph[kRG][2], pl[kRG][2];
+  // M(u): scores of tile u, P.V of tile u-1 (matrix cores)
+  auto m_half = [&](int u, auto ub) __attribute__((always_inline)) {
+    constexpr int UB = decltype(ub)::value;  // u % 2
+    __builtin_amdgcn_s_setprio(1);
+    if (u < n_compute) qk(s_k[UB], sc);
+    if (u >= 1 && u - 1 < n_compute) pv(ph, pl, s_v[1 - UB]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // V(t): row maxima and probabilities of tile t (vector ALU)
+  auto v_half = [&](int t) __attribute__((always_inline)) {
+    if (t >= 0 && t < n_compute) {
       row_max(t, sc);
-      exp_pv(sc, s_v[b]);
-    }
-    // Tile t+1's loads (issued as this tile began, into buffers 1 - b) have
-    // had this tile's work to land; the barrier publishes them and tells
-    // every wave that buffers b are free again.
-    wait_lds_loads();
-    if (t + 1 < ntiles) zero_v_tail(s_v[1 - b], t + 1);
-    __syncthreads();
-    if (t + 2 < ntiles) {
-      load_lds(t + 2, ids, 0, false, s_k[b]);
-      load_lds(t + 2, ids, kv_half, true, s_v[b]);
+      make_p(sc, ph, pl);
     }
   };
-  using yes = std::true_type;
-  using no = std::false_type;
-  const int n_compute = min(ntiles, w_last_tile + 1);  // tiles with work for this wave (uniform)
-  int t = 0;
-  for (; t + 1 < n_compute; t += 2) {
-    step(t, buf0{}, yes{});
-    step(t + 1, buf1{}, yes{});
-  }
-  if (t < n_compute) {
-    step(t, buf0{}, yes{});
-    ++t;
-  }
-  for (; t < ntiles; ++t) {
-    if (t & 1)
-      step(t, buf1{}, no{});
-    else
-      step(t, buf0{}, no{});
-  }
+  // half-phases 2u and 2u+1 for wave group WG
+  auto tile2 = [&](int u, auto ub, auto g) __attribute__((always_inline)) {
+    constexpr int UB = decltype(ub)::value;
+    constexpr int WG = decltype(g)::value;
+    if (u + 1 < ntiles) load_lds(u + 1, ids_k, 0, false, s_k[1 - UB]);
+    if (u < ntiles) load_lds(u, ids_v, kv_half, true, s_v[UB]);
+    if constexpr (WG == 0) m_half(u, ub);
+    else v_half(u - 1);
+    __syncthreads();
+    if constexpr (WG == 0) v_half(u);
+    else m_half(u, ub);
+    if (u + 2 < ntiles) fetch_ids(u + 2, ids_k);
+    if (u + 1 < ntiles) fetch_ids(u + 1, ids_v);
+    wait_lds_loads();
+    if (u < ntiles) zero_v_tail(s_v[UB], u);
+    __syncthreads();
+  };
+  using b0 = std::integral_constant<int, 0>;
+  using b1 = std::integral_constant<int, 1>;
+  auto run = [&](auto g) __attribute__((always_inline)) {
+    int u = 0;
+    for (; u + 1 <= ntiles; u += 2) {
+      tile2(u, b0{}, g);
+      tile2(u + 1, b1{}, g);
+    }
+    if (u <= ntiles) tile2(u, b0{}, g);
+  };
+  if (grp1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
   const bool seq_poisoned = poisoned;
 
   // ---- normalise and store: lane holds rows 4*grp + jj of each group, columns 16*nt + r16
