@@ -369,15 +369,28 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) sacc[rg][kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // The K operands of step kc+1 are read while step kc's MFMAs run (order
+    // pinned: step 0's reads, then per step the next step's 4 reads and this
+    // step's 4 kRG MFMAs).
+    u32x4_t ka[2][4];
+    auto rdk = [&](int kc, u32x4_t (&a)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc)
+      for (int kt = 0; kt < 4; ++kt) a[kt] = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
+    };
+    rdk(0, ka[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // step 0's reads first
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&kt_lds[k_base[kc] + 16 * kt * C::ROWB]);
+    for (int kc = 0; kc < C::KC; ++kc) {
+      if (kc + 1 < C::KC) rdk(kc + 1, ka[(kc + 1) & 1]);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
-          sacc[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
-      }
+          sacc[rg][kt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc & 1][kt]), qb[rg][kc], sacc[rg][kt], 0, 0, 0);
+      if (kc + 1 < C::KC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kRG, 0);                 // MFMAs
+    }
   };
   // Softmax, first half: mask tile t's raw scores in place (diagonal tiles
   // only), take each row's maximum and raise the running maximum, rescaling
@@ -432,7 +445,8 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   };
   // Softmax, second half: P = exp2(cs * s - m) in fp32 (the permuted key
   // order), split into bf16 parts P_hi + P_lo (P_hi the truncation, P_lo the
-  // rounded remainder); the row sums P 1 on the matrix cores, part by part.
+  // rounded remainder).  Their row sums P 1 are taken with P.V, on the matrix
+  // cores, so the vector half ends with its last vector instruction.
   auto make_p = [&](const f32x4_t (&sacc)[kRG][4], bf16x8_t (&ph)[kRG][2], bf16x8_t (&pl)[kRG][2])
                     __attribute__((always_inline)) {
 #pragma unroll
@@ -456,14 +470,9 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         ph[rg][ks] = as_bf16x8(hi);
         pl[rg][ks] = as_bf16x8(lo);
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
-        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], ones, osum[rg], 0, 0, 0);
-      }
     }
   };
-  // O += P V: P_hi then P_lo against each V operand.
+  // O += P V and the row sums += P 1: P_hi then P_lo against each operand.
   auto pv = [&](const bf16x8_t (&ph)[kRG][2], const bf16x8_t (&pl)[kRG][2], const char *vt_lds)
                 __attribute__((always_inline)) {
     // V operands are read kVAhead steps before the MFMAs that use them, and
@@ -482,6 +491,14 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     };
 #pragma unroll
     for (int st = 0; st < kVAhead; ++st) vq[st] = rdv(st);
+    // the row sums P 1 (they need no V operand, so they run while the first reads land)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rg][ks], ones, osum[rg], 0, 0, 0);
+        osum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rg][ks], ones, osum[rg], 0, 0, 0);
+      }
     // Steps go in pairs (output tiles nt, nt+1 of one key half): the P_hi
     // and P_lo products into one tile are 2 kRG MFMAs apart.
 #pragma unroll
@@ -509,8 +526,9 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
 
   // ---- ping-pong.  Waves w and w + 4 share a SIMD (a workgroup's waves go
   // to its CU's four SIMDs in turn).  Each wave alternates a matrix-core half
-  // (scores of tile t, P.V of tile t-1) and a vector half (row maxima and
-  // probabilities of tile t); waves 4-7 run one half-phase behind waves 0-3,
+  // (scores of tile t, P.V and row sums of tile t-1) and a vector half (row
+  // maxima and probabilities of tile t); waves 4-7 run one half-phase behind
+  // waves 0-3,
   // so while one wave of a SIMD feeds the matrix cores the other runs its
   // softmax, instead of both meeting in the same phase.  The matrix-core
   // halves run at raised wave priority, so the arbiter gives an MFMA the issue
@@ -531,7 +549,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   __syncthreads();
   f32x4_t sc[kRG][4];
   bf16x8_t ph[kRG][2], pl[kRG][2];
-  // M(u): scores of tile u, P.V of tile u-1 (matrix cores)
+  // M(u): scores of tile u, P.V and row sums of tile u-1 (matrix cores)
   auto m_half = [&](int u, auto ub) __attribute__((always_inline)) {
     constexpr int UB = decltype(ub)::value;  // u % 2
     __builtin_amdgcn_s_setprio(1);
