@@ -62,6 +62,42 @@ def test_noalloc_matches_pa_decode_on_two_calls(dtype, group):
         assert err <= ATOL
 
 
+def test_noalloc_work_list_path_on_two_calls():
+    """Batches of 1,024 or more (sequence, KV head) pairs spanning several
+    partitions take the work-list decode, whose item list and take counter
+    also live in the static array: two such calls in a row (the second with
+    fewer pairs) against pa_decode with a workspace, and against the oracle."""
+    from oracle.parallel import run_tasks, sequence_task
+    rng = np.random.default_rng(4242)
+    for i, S in enumerate((136, 128)):  # 1,088 then 1,024 pairs at 8 KV heads
+        lens = np.clip(np.round(rng.lognormal(np.log(300), 1.0, size=S)), 1, 3000).astype(np.int64)
+        lens[::17] = 1
+        w = make_custom(name=f"noalloc-list-{i}", seed=4300 + i, dtype="bf16",
+                        num_blocks=int(sum(-(-int(L) // 16) for L in lens)) + 16, num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, lengths=lens, num_steps=1)
+        st = w.steps[0]
+        pool = device_pool(w)
+        q, tables, lens_d = to_dev(st.q, w.dtype), i32(w.block_tables), i32(st.context_lens)
+        mcl = int(st.context_lens.max())
+        part = 512
+        need = pa.pa_decode_workspace_size(pool, S, 32, mcl, part)
+        say(f"[noalloc list] call {i + 1}: S={S} pairs={S * 8} partitions of {part} (max len {mcl}), "
+            f"partials and list {need} B")
+        assert 0 < need <= 32 << 20
+        out = torch.full((S, 32, 128), 7.0, device=pool.device)
+        assert noalloc(pool, q, tables, lens_d, w.scale, mcl, part, out) == 0
+        ref = pa.pa_decode(pool, q, tables, lens_d, scale=float(w.scale), max_context_len=mcl, partition_size=part,
+                           workspace=torch.empty(need, dtype=torch.uint8, device=pool.device))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        got = out.cpu().numpy()
+        want = run_tasks(sequence_task(w.pool, w.block_tables[s], int(st.context_lens[s]), st.q[s], float(w.scale))
+                         for s in range(S))
+        err = max(float(np.abs(got[s].astype(np.float64) - wv).max()) for s, wv in enumerate(want))
+        say(f"    bit-identical to pa_decode; every row vs oracle: max abs err {err:.3e}")
+        assert err <= ATOL
+
+
 def test_noalloc_single_partition_and_empty_batch():
     w = make_custom(name="noalloc-short", seed=97, dtype="bf16", num_blocks=40, num_q_heads=8, num_kv_heads=2,
                     head_dim=64, block_size=16, lengths=[100, 5, 300])
