@@ -470,7 +470,29 @@ def _random_case(seed):
     return G, D, B, dtype, hkv, lens, part, keep
 
 
-@pytest.mark.parametrize("seed", list(range(12)))
+@pytest.mark.parametrize("group", [4, 8])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 5.0])
+def test_decode_any_scale(scale, group):
+    # the scale is any float: negative (the softmax favours the smallest q.k), zero (a
+    # uniform average over the context) and large (a near-argmax softmax whose running
+    # maximum jumps by hundreds of log2 units); vector scores (group 4) and matrix-core
+    # scores (group 8), several partitions, against the oracle at the same scale
+    lens = np.array([1, 700, 33, 1500, 256], dtype=np.int64)
+    hkv = 2
+    w = make_custom(name=f"scale-{scale}-g{group}", seed=131 + group, dtype="bf16",
+                    num_blocks=int(sum(-(-int(L) // 16) for L in lens)) + 4, num_q_heads=hkv * group,
+                    num_kv_heads=hkv, head_dim=128, block_size=16, lengths=lens)
+    w.scale = np.float32(scale)
+    st = w.steps[0]
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    for part in (0, 256):
+        got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, part)
+        err = np.abs(got - want).max()
+        say(f"[scale {scale}] G={group} partition={part}: max abs err {err:.3e}")
+        assert np.isfinite(got).all() and err <= ATOL
+
+
+@pytest.mark.parametrize("seed", list(range(40)))
 def test_decode_seeded_random_shapes(seed):
     # one seeded draw of every supported knob at a time: group, head dim, block size, dtype,
     # KV heads, ragged lengths, partition size and cache policy, against the oracle

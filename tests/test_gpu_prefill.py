@@ -38,6 +38,22 @@ def oracle_pool(w):
     return paged.cache_write_ref(w.pool, w.k_new, w.v_new, slots)
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 5.0])
+def test_prefill_any_scale(scale):
+    # negative (applied as |scale| on -Q), zero (a uniform average over each row's visible
+    # keys) and large (near-argmax, the running maximum raised by hundreds of log2 units)
+    w = make_prefill_custom(name=f"prefill-scale-{scale}", seed=141, dtype="bf16", num_blocks=200,
+                            num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                            context_lens=[300, 1000, 77], chunk_lens=[300, 130, 77])
+    w.scale = np.float32(scale)
+    pool, got = gpu_prefill(w)
+    pool_np = oracle_pool(w)
+    want = paged.prefill_ref(pool_np, w.q, w.query_start_loc, w.context_lens, w.block_tables, float(w.scale))
+    err = np.abs(got.astype(np.float64) - want).max()
+    say(f"[prefill scale {scale}] max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
+
+
 @pytest.mark.parametrize("k", [1, 2])
 def test_prefill_small_workloads_match_oracle(k):
     w = make_prefill(k, small=True)
