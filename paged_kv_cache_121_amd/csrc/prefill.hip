@@ -528,17 +528,16 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // to its CU's four SIMDs in turn).  Each wave alternates a matrix-core half
   // (scores of tile t, P.V and row sums of tile t-1) and a vector half (row
   // maxima and probabilities of tile t); waves 4-7 run one half-phase behind
-  // waves 0-3,
-  // so while one wave of a SIMD feeds the matrix cores the other runs its
-  // softmax, instead of both meeting in the same phase.  The matrix-core
-  // halves run at raised wave priority, so the arbiter gives an MFMA the issue
-  // slot before the other wave's vector instruction (2 % measured).  Every
-  // half-phase ends in a barrier.  Half-phase
-  // h = 2u (even) starts the loads of K(u+1) (buffer (u+1) % 2) and V(u)
-  // (buffer u % 2); half-phase 2u+1 waits for them before its barrier.  Wave
-  // group 0 runs M(u) in half-phase 2u and V(u) in 2u+1; group 1 runs M(u)
-  // in 2u+1 and V(u) in 2u+2.  K(u) and V(u-1) are read in M(u) only, so
-  // their buffers are free after half-phase 2u+1.
+  // waves 0-3, so while one wave of a SIMD feeds the matrix cores the other
+  // runs its softmax, instead of both meeting in the same phase.  The
+  // matrix-core halves run at raised wave priority, so the arbiter gives an
+  // MFMA the issue slot before the other wave's vector instruction (2 %
+  // measured).  Every half-phase ends in a barrier.  Half-phase h = 2u
+  // (even) starts the loads of K(u+1) (buffer (u+1) % 2) and V(u) (buffer
+  // u % 2); half-phase 2u+1 waits for them before its barrier.  Wave group 0
+  // runs M(u) in half-phase 2u and V(u) in 2u+1; group 1 runs M(u) in 2u+1
+  // and V(u) in 2u+2.  K(u) and V(u-1) are read in M(u) only, so their
+  // buffers are free after half-phase 2u+1.
   const int n_compute = min(ntiles, w_last_tile + 1);  // tiles with work for this wave (uniform)
   const int grp1 = wave >= kPfWaves / 2;
   int ids_k[NBT], ids_v[NBT];
