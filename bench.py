@@ -32,7 +32,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="1-5 (default: 2, the Qwen3-8B batch-64 layer)")
+    ap.add_argument("--workload", type=str, default="2", choices=["1", "2", "3", "4", "5", "4tp8"],
+                    help="1-5 (default: 2, the Qwen3-8B batch-64 layer), or 4tp8: one GPU's share of workload 4 "
+                         "at 8-way tensor parallelism (1 KV head, 8 query heads)")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--decode-reps", type=int, default=50, help="timed decode-only launches for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -84,7 +86,7 @@ def _traffic_json(path: str):
     return json.loads(text[start + 7:text.index("```", start + 7)])
 
 
-def measured_traffic(workload: int, partition_size: int):
+def measured_traffic(workload: str, partition_size: int):
     """HBM bytes per decode launch from the committed counter summary, if it was
     taken on the current decode kernel source at this partition size; else None."""
     t = _traffic_json(TRAFFIC_FILE)
@@ -747,7 +749,7 @@ def main():
     import torch
 
     import paged_kv_cache_121_amd as pa
-    from workloads import CONFIG_NAMES, make_config
+    from workloads import CONFIG_NAMES, make_config, make_tp_share
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -786,7 +788,7 @@ def main():
                           "sampled_max_abs_err": r["sampled_max_abs_err"]}), flush=True)
         return
     t_gen = time.perf_counter()
-    w = make_config(args.workload)
+    w = make_tp_share(8) if args.workload == "4tp8" else make_config(int(args.workload))
     t_gen = time.perf_counter() - t_gen
     st = w.steps[0]
     print(f"[bench] workload {args.workload}: {w.name} generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -900,7 +902,9 @@ def main():
         "dtype": {"bf16": "bf16 K/V and Q, fp32 accumulate", "f32": "f32"}[w.dtype],
         "data": "synthetic (seeded N(0,1) K/V/Q; lengths, placement and sharing per the workload recipe)",
         "config": {
-            "workload": f"workload {args.workload}: {CONFIG_NAMES[args.workload]}",
+            "workload": f"workload {args.workload}: " + (
+                CONFIG_NAMES[4] + "; one GPU's share at 8-way tensor parallelism: 1 KV head, 8 query heads"
+                if args.workload == "4tp8" else CONFIG_NAMES[int(args.workload)]),
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": w.num_blocks,
             "context_tokens": int(st.context_lens.sum()), "max_context_len": max_len,
