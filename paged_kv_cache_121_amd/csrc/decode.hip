@@ -406,17 +406,25 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.0f;
 
-  const int nb_w = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
-  const int nch = nb_w * CPB;
+  // The partition's stages of CH tokens (up to the last that holds a token of
+  // the context) are dealt to the waves in turn: wave w takes stages w,
+  // w + kWaves, ...  With blocks longer than a stage the waves thus share a
+  // block instead of taking whole blocks (33 blocks of 128 tokens over 4
+  // waves would leave one wave a ninth block).
+  static_assert(C::UNIT == CPB * CH, "a unit is CPB stages: stage g starts at token g * CH");
+  const int part_len = min(L - blk_begin * B, nunits * C::UNIT);  // tokens of this partition
+  const int nstages = (part_len + CH - 1) / CH;
+  const int nch = nstages > wave ? (nstages - wave + kWaves - 1) / kWaves : 0;
   const char *kv_head_base = pool + (int64_t)h * C::TILE;
   const int64_t v_off = (int64_t)num_kv_heads * C::TILE;
   const int lane_off = lane * C::VEC;
 
   auto issue = [&](int ci, Frag<KW> (&kf)[KN], Frag<NW> (&vf)[NS]) {
-    const int unit = wave + (ci / CPB) * kWaves;
+    const int g = wave + ci * kWaves;  // this stage's index in the partition
+    const int unit = g / CPB;
     if constexpr (MQ) {
       // K: token col, bytes 64 kc + 16 row of its row; V: token 4 row + i, dims col * EPL ...
-      const int sub = ci % CPB;
+      const int sub = g % CPB;
       const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
       const char *cp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK;
       const char *kp = cp + col * C::ROW + 16 * row;
@@ -426,7 +434,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
 #pragma unroll
       for (int i = 0; i < NS; ++i) load_frag<NW, NT>(vf[i], vp + i * C::ROW);
     } else if constexpr (R == 1) {
-      const int sub = ci % CPB;
+      const int sub = g % CPB;
       const int phys = __builtin_amdgcn_readfirstlane(s_tbl[unit]);
       const char *kp = kv_head_base + (int64_t)phys * (2 * v_off) + sub * C::CHUNK + lane_off;
 #pragma unroll
@@ -450,7 +458,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // (each layout's body is instantiated only for its own kernels)
   auto process_mq = [&](int ci, const auto &kf, const auto &vf) {
     if constexpr (MQ) {
-      const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
+      const int tok0 = blk_begin * B + (wave + ci * kWaves) * CH;
       const bool partial = tok0 + CH > L;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -499,7 +507,7 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     }
   };
   auto process_vec = [&](int ci, const auto &kf, const auto &vf) {
-    const int tok0 = blk_begin * B + (wave + (ci / CPB) * kWaves) * C::UNIT + (ci % CPB) * CH;
+    const int tok0 = blk_begin * B + (wave + ci * kWaves) * CH;
     const bool partial = tok0 + CH > L;
     // QK for the 4 tokens this row sees in the chunk
     float sc[NS][HPL];
