@@ -212,7 +212,7 @@ int32_t pa_decode_partition_size(const pa_pool *pool, int32_t num_seqs, int32_t 
  * a negative
  * pa_status for arguments pa_decode would refuse (a bad pool, negative
  * sizes, num_q_heads not a multiple of num_kv_heads, a partition_size that
- * is not a multiple of max(block_size, 16) or exceeds 512 blocks).  The pool
+ * is not a multiple of max(block_size, 16) or exceeds 2,048 blocks).  The pool
  * descriptor stands for the separate KV-head count and head size of a plain
  * shape signature (it also fixes the block size, which the automatic
  * partition depends on), and partition_size is the one pa_decode will get,
@@ -235,7 +235,7 @@ int64_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t 
  *   max_context_len : host-known upper bound of context_lens.
  *   partition_size  : tokens per split-context partition; 0 = automatic;
  *                  else a positive multiple of max(block_size, 16), at
- *                  most 512 blocks.
+ *                  most 2,048 blocks.
  *   flags        : PA_DECODE_STREAM or PA_DECODE_KEEP_CACHED (see above).
  *   workspace    : scratch for split-context partial results, at least
  *                  pa_decode_workspace_size() bytes, 256-byte aligned (may

@@ -309,7 +309,10 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   static_assert(B % 4 == 0 && (B < CH ? CH % B == 0 : B % CH == 0), "block size");
   static_assert(!MQ || (!std::is_same_v<T, float> && G == 8 && CH == 16 && B >= CH), "matrix-core layout");
 
-  __shared__ int s_tbl[kMaxPartitionBlocks];
+  // Partition length cap in blocks (the host routes longer partitions to the
+  // grid launch).
+  constexpr int kTblCap = LIST ? kMaxListPartitionBlocks : kMaxPartitionBlocks;
+  __shared__ int s_tbl[kTblCap];
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
@@ -349,14 +352,21 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
     for (int r = 0; r < G; ++r)
       load_frag<NW>(qf[r], q + ((head_row0 + (r ^ sigma)) * D + col * EPL) * C::kElem);
   }
-  static_assert(kMaxPartitionBlocks <= 2 * kThreads, "two table entries per thread");
+  // Table entries staged per thread; up to two are loaded early (in
+  // registers), any further ones (grid partitions of more than 2 kThreads
+  // blocks, i.e. small blocks) once the length is known, straight into LDS.
+  constexpr int kTblPerThread = (kTblCap + kThreads - 1) / kThreads;
+  constexpr int kTblEarly = kTblPerThread < 2 ? kTblPerThread : 2;
   const int blk_begin = p * part_blocks;
   const int32_t *trow = tables + (int64_t)s * max_blocks_per_seq + blk_begin;
-  int tb[2] = {0, 0};
+  int tb[kTblEarly];
+#pragma unroll
+  for (int k = 0; k < kTblEarly; ++k) tb[k] = 0;
   if (p == 0) {
     const int n = min(part_blocks, max_blocks_per_seq);
-    if (tid < n) tb[0] = trow[tid];
-    if (tid + kThreads < n) tb[1] = trow[tid + kThreads];
+#pragma unroll
+    for (int k = 0; k < kTblEarly; ++k)
+      if (tid + k * kThreads < n) tb[k] = trow[tid + k * kThreads];
   }
 
   const int L = context_lens[s];
@@ -379,17 +389,24 @@ decode_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_head
   // Partitions hold whole units, so nunits * R <= part_blocks.
   const int nunits = (nblk + R - 1) / R;
   bool bad = false;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kThreads;
+  auto stage = [&](int i, int b) {
     if (i < nunits * R) {
-      int b = i >= nblk ? 0 : p == 0 ? tb[k] : trow[i];
+      if (i >= nblk) b = 0;
       if (b < 0 || (int64_t)b >= num_blocks) {
         bad = true;
         b = 0;
       }
       s_tbl[i] = b;
     }
+  };
+#pragma unroll
+  for (int k = 0; k < kTblEarly; ++k) {
+    const int i = tid + k * kThreads;
+    stage(i, p == 0 ? tb[k] : i < nblk ? trow[i] : 0);
+  }
+  if constexpr (kTblPerThread > kTblEarly) {
+#pragma unroll 1
+    for (int i = tid + kTblEarly * kThreads; i < nunits * R; i += kThreads) stage(i, i < nblk ? trow[i] : 0);
   }
   const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;  // all lanes take part
   if (lane == 0) s_bad[wave] = wave_bad;

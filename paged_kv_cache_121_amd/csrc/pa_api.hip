@@ -287,7 +287,7 @@ int prepare_decode(const pa_pool *pool, const void *q, float *out, const int32_t
   a->num_partitions = parts;
   a->stream_loads = (flags & PA_DECODE_KEEP_CACHED) == 0;
   *ws_need = decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts,
-                                     decode_uses_work_list(num_seqs, d.num_kv_heads, parts))
+                                     decode_uses_work_list(num_seqs, d.num_kv_heads, parts, a->partition_blocks))
                   .total;
   return PA_OK;
 }
@@ -295,7 +295,8 @@ int prepare_decode(const pa_pool *pool, const void *q, float *out, const int32_t
 // Points the split-context partials and the work list of `a` into a
 // workspace of the size prepare_decode asked for (256-byte aligned).
 void bind_workspace(DecodeArgs *a, char *base) {
-  const bool list = decode_uses_work_list(a->num_seqs, a->pool.num_kv_heads, a->num_partitions);
+  const bool list =
+      decode_uses_work_list(a->num_seqs, a->pool.num_kv_heads, a->num_partitions, a->partition_blocks);
   const WorkspaceLayout w = decode_workspace_layout(a->num_seqs, a->num_q_heads, a->pool.num_kv_heads,
                                                     a->pool.head_dim, a->num_partitions, list);
   if (a->num_partitions > 1) {
@@ -375,8 +376,9 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_k
   return w;
 }
 
-bool decode_uses_work_list(int num_seqs, int num_kv_heads, int num_partitions) {
-  return num_partitions > 1 && (int64_t)num_seqs * num_kv_heads >= kManyPairs;
+bool decode_uses_work_list(int num_seqs, int num_kv_heads, int num_partitions, int partition_blocks) {
+  return num_partitions > 1 && (int64_t)num_seqs * num_kv_heads >= kManyPairs &&
+         partition_blocks <= kMaxListPartitionBlocks;
 }
 
 }  // namespace pa
@@ -516,7 +518,7 @@ int64_t pa_decode_workspace_size(const pa_pool *pool, int32_t num_seqs, int32_t 
   if (num_seqs == 0) return 0;
   const int parts = max_context_len == 0 ? 1 : (max_context_len + part - 1) / part;  // as pa_decode
   return (int64_t)decode_workspace_layout(num_seqs, num_q_heads, d.num_kv_heads, d.head_dim, parts,
-                                          decode_uses_work_list(num_seqs, d.num_kv_heads, parts))
+                                          decode_uses_work_list(num_seqs, d.num_kv_heads, parts, part / d.block_size))
       .total;
 }
 

@@ -10,8 +10,12 @@
 
 namespace pa {
 
-// Largest partition, in blocks, whose table entries one workgroup stages in LDS.
-constexpr int kMaxPartitionBlocks = 512;
+// Largest partition, in blocks, whose table entries one workgroup stages in
+// LDS: 2,048 for a grid launch, 512 for a work-list launch (whose persistent
+// workgroups pay for every extra register and LDS byte in residency; calls
+// with longer partitions take the grid).
+constexpr int kMaxPartitionBlocks = 2048;
+constexpr int kMaxListPartitionBlocks = 512;
 // Query rows (GQA head x token) one prefill workgroup takes: 16 per row group,
 // two groups per wave, 8 waves.
 constexpr int kPrefillRowGroups = 2;
@@ -80,7 +84,7 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int num_q_heads, int num_k
 // span several partitions (measured: 5-6 % faster on 512 lognormal contexts;
 // a batch of 1,024 pairs of at most one partition each is 10 % slower with
 // the list's prepass than with the grid).
-bool decode_uses_work_list(int num_seqs, int num_kv_heads, int num_partitions);
+bool decode_uses_work_list(int num_seqs, int num_kv_heads, int num_partitions, int partition_blocks);
 
 hipError_t launch_slot_mapping(const PoolDesc &pool, const int32_t *tables, int max_blocks_per_seq,
                                int num_seqs, const int32_t *seq_ids, const int32_t *positions,

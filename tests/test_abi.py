@@ -111,7 +111,16 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.pa_decode_workspace_size(ref(good), 3, 6, 1024, 16) == -1  # Hq not a multiple of Hkv
     assert lib.pa_decode_workspace_size(ref(good), -1, 4, 1024, 16) == -1
     assert lib.pa_decode_workspace_size(ref(pa.pa_pool(0x1000, 16, 4, 12, 64, 0)), 3, 4, 1024, 16) == -2
-    assert lib.pa_decode_workspace_size(ref(good), 3, 4, 1 << 20, 16 * 513) == -2  # over 512 blocks
+    assert lib.pa_decode_workspace_size(ref(good), 3, 4, 1 << 20, 16 * 2049) == -2  # over 2,048 blocks
+    # 1,024 (sequence, KV head) pairs of several partitions walk a work list (one int32 per
+    # (pair, partition) plus a 256-byte counter region) while a partition holds at most 512
+    # blocks; longer partitions take the grid, whose workspace is the partials alone
+    many = pa.pa_pool(0x1000, 1 << 16, 8, 16, 64, pa.PA_BF16)
+    list_ws = lib.pa_decode_workspace_size(ref(many), 128, 8, 20000, 16 * 512)
+    grid_ws = lib.pa_decode_workspace_size(ref(many), 128, 8, 20000, 16 * 513)
+    partials = 1024 * 3 * 64 * 4 + 1024 * 3 * 2 * 4   # 3 partitions either way, 256-aligned sizes
+    assert grid_ws == partials
+    assert list_ws == partials + 1024 * 3 * 4 + 256
 
 
 def test_checked_mode_leaves_scalar_errors_and_no_ops_on_the_host(monkeypatch):

@@ -452,6 +452,47 @@ def test_decode_work_shapes_by_partition(group, dtype, partition_size):
     assert np.isfinite(got).all() and np.abs(got - want).max() <= ATOL
 
 
+@pytest.mark.parametrize("group,dtype,block_size,partition_size", [
+    (4, "bf16", 4, 8192), (8, "bf16", 4, 4096), (1, "f32", 8, 8192), (2, "bf16", 4, 2048), (4, "f32", 4, 1536)])
+def test_decode_long_partitions_of_small_blocks(group, dtype, block_size, partition_size):
+    # partitions of up to 2,048 blocks: a workgroup stages two table entries per thread
+    # early and the rest (up to six more per thread) in a second pass
+    hkv = 2
+    lens = np.array([2 * partition_size + 3, 9000, partition_size, partition_size + 1, 1, 700, 4100], dtype=np.int64)
+    nb = int(sum(-(-L // block_size) for L in lens)) + 4
+    w = make_custom(name="long-partitions", seed=97 + block_size + group, dtype=dtype, num_blocks=nb,
+                    num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=128, block_size=block_size, lengths=lens)
+    st = w.steps[0]
+    say(f"[long partitions] G={group} {dtype} B={block_size} partition {partition_size} "
+        f"({partition_size // block_size} blocks)")
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, partition_size)
+    err = np.abs(got - want).max()
+    say(f"    max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL
+
+
+def test_decode_many_pairs_with_long_partitions():
+    # 1,024 (sequence, KV head) pairs of several partitions would walk a work list, whose
+    # workgroups stage at most 512 table entries: 1,024-block partitions take the grid
+    # instead, 512-block ones the list; both against the oracle
+    rng = np.random.default_rng(2024)
+    S, hkv, B = 128, 8, 4
+    lens = np.clip(np.rint(rng.lognormal(np.log(40), 0.8, size=S)), 1, 400).astype(np.int64)
+    lens[7], lens[90] = 5000, 4097
+    nb = int(sum(-(-L // B) for L in lens)) + 4
+    w = make_custom(name="many-pairs-long-partitions", seed=131, dtype="bf16", num_blocks=nb,
+                    num_q_heads=hkv, num_kv_heads=hkv, head_dim=64, block_size=B, lengths=lens)
+    st = w.steps[0]
+    say(f"[many pairs] {S} sequences x {hkv} KV heads, B={B}, max {lens.max()}")
+    want = paged.decode_ref(w.pool, st.q, w.block_tables, st.context_lens, float(w.scale))
+    for part in (4096, 2048):
+        got = _decode_custom(w, w.pool, w.block_tables, st.context_lens, st.q, part)
+        err = np.abs(got - want).max()
+        say(f"    partition {part} ({part // B} blocks): max abs err {err:.3e}")
+        assert np.isfinite(got).all() and err <= ATOL
+
+
 # ------------------------------------------------------------------ seeded random shapes
 
 
