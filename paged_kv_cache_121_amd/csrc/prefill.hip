@@ -228,10 +228,14 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   bool poisoned = false;
 
   // K and V go straight from global memory into LDS (global_load_lds_dwordx4:
-  // each instruction writes 1 KiB, lane l's 16 bytes at l * 16).  Instruction i
-  // of wave w fills tile rows RPI*(8i+w) .. +RPI-1; lane l writes slot l % NCH16
-  // of row RPI*(8i+w) + l / NCH16, and loads the chunk its tile's swizzle puts
-  // in that slot (K: 16-byte XOR swizzle, V: v_lds8).  Keys past the context
+  // each instruction writes 1 KiB, lane l's 16 bytes at l * 16).  Waves 4-7
+  // (the loaders) issue every load of a tile: instruction i of loader lw fills
+  // tile rows RPI*(4i+lw) .. +RPI-1; lane l writes slot l % NCH16 of row
+  // RPI*(4i+lw) + l / NCH16, and loads the chunk its tile's swizzle puts in
+  // that slot (K: 16-byte XOR swizzle, V: v_lds8).  The loaders start a tile
+  // in their vector half, so the matrix-core waves 0-3 are not held up behind
+  // a CU's worth of loads queueing for the texture path at the tile's start
+  // (1-2.5 % faster than every wave loading its own rows).  Keys past the context
   // are loaded from wherever their rows fall (the last block's tail, or block
   // 0 past the table's used entries): their scores are masked before any use
   // and zero_v_tail overwrites their values with zeros (a zero probability
@@ -246,10 +250,13 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     return is_v ? slot ^ (2 * (row % (C::NCH8 / 4))) : slot ^ (row % C::NCH16);
   };
   // this lane's byte offset inside an instruction's RPI rows
-  uint32_t lane_off_k[C::LOADS], lane_off_v[C::LOADS];
+  constexpr int kLoaders = kPfWaves / 2;               // waves 4-7
+  constexpr int LPW = C::LOADS * kPfWaves / kLoaders;  // load instructions per loader per tile
+  const int lw = wave % kLoaders;
+  uint32_t lane_off_k[LPW], lane_off_v[LPW];
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int row = RPI * (kPfWaves * i + wave) + dl_row;
+  for (int i = 0; i < LPW; ++i) {
+    const int row = RPI * (kLoaders * i + lw) + dl_row;
     lane_off_k[i] = dl_row * C::ROWB + (src_chunk(row, dl_slot, false) << 4);
     lane_off_v[i] = dl_row * C::ROWB + (src_chunk(row, dl_slot, true) << 4);
   }
@@ -261,7 +268,9 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       ids[i] = __builtin_amdgcn_readfirstlane(jb < seq_blocks ? table_row[jb] : 0);
     }
   };
-  auto load_lds = [&](int t, const int (&ids)[NBT], int64_t part_off, bool is_v, char *buf)
+  // Every wave checks the tile's block ids (an invalid id poisons its rows);
+  // only a loader (`issue`) starts the loads.
+  auto load_lds = [&](int t, const int (&ids)[NBT], int64_t part_off, bool is_v, char *buf, bool issue)
                       __attribute__((always_inline)) {
     int blk[NBT];
 #pragma unroll
@@ -273,14 +282,15 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       }
       blk[i] = b;
     }
+    if (!issue) return;
     if constexpr (RPI <= B) {
       // Every instruction's RPI rows lie in one block, so its address is a
       // uniform base (scalar registers) plus this lane's fixed offset.  Rows
       // past the context read whatever the block holds there: their scores
       // are masked, and zero_v_tail zeroes their values.
 #pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) {
-        const int row0 = RPI * (kPfWaves * i + wave);  // uniform
+      for (int i = 0; i < LPW; ++i) {
+        const int row0 = RPI * (kLoaders * i + lw);  // uniform
         int b, rib0;
         if constexpr (B > kKeys) {
           b = blk[0];
@@ -298,7 +308,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         const char *sbase = reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
         const uint32_t off = is_v ? lane_off_v[i] : lane_off_k[i];
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(sbase + off),
-                                         (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
+                                         (__attribute__((address_space(3))) void *)(buf + (kLoaders * i + lw) * 1024),
                                          16, 0, 0);
       }
     } else {
@@ -306,8 +316,8 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
       // addresses; rows past the context read the last real row
       const int last_row = ctx - 1 - t * kKeys;
 #pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) {
-        const int row = RPI * (kPfWaves * i + wave) + dl_row;
+      for (int i = 0; i < LPW; ++i) {
+        const int row = RPI * (kLoaders * i + lw) + dl_row;
         const int chunk = src_chunk(row, dl_slot, is_v);
         const int src_row = min(row, last_row);
         const int slot = src_row / B;
@@ -316,23 +326,24 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
         for (int k = 1; k < NBT; ++k) b = slot == k ? blk[k] : b;
         const char *src = head_base + (int64_t)b * 2 * kv_half + part_off + (src_row % B) * C::ROWB + chunk * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                         (__attribute__((address_space(3))) void *)(buf + (kPfWaves * i + wave) * 1024),
+                                         (__attribute__((address_space(3))) void *)(buf + (kLoaders * i + lw) * 1024),
                                          16, 0, 0);
       }
     }
   };
   // Rows of V tile t past the context hold whatever their source rows held
-  // (padding may be NaN); each lane overwrites the 16 bytes its own loads put
-  // there with zeros.  Only the tile where the context ends has such rows
-  // (uniform test); call after this wave's loads of the tile have landed.
+  // (padding may be NaN); each loader lane overwrites the 16 bytes its own
+  // loads put there with zeros.  Only the tile where the context ends has such
+  // rows (uniform test); a loader calls it after its loads of the tile have
+  // landed.
   auto zero_v_tail = [&](char *buf, int t) __attribute__((always_inline)) {
     const int vrows = ctx - t * kKeys;  // rows of the tile inside the context (uniform)
     if (vrows < kKeys) {
 #pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) {
-        const int row = RPI * (kPfWaves * i + wave) + dl_row;
+      for (int i = 0; i < LPW; ++i) {
+        const int row = RPI * (kLoaders * i + lw) + dl_row;
         if (row >= vrows)
-          *reinterpret_cast<u32x4_t *>(&buf[(kPfWaves * i + wave) * 1024 + lane * 16]) = u32x4_t{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t *>(&buf[(kLoaders * i + lw) * 1024 + lane * 16]) = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -532,17 +543,20 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // runs its softmax, instead of both meeting in the same phase.  The
   // matrix-core halves run at raised wave priority, so the arbiter gives an
   // MFMA the issue slot before the other wave's vector instruction (2 %
-  // measured).  Every half-phase ends in a barrier.  Half-phase h = 2u
-  // (even) starts the loads of K(u+1) (buffer (u+1) % 2) and V(u) (buffer
-  // u % 2); half-phase 2u+1 waits for them before its barrier.  Wave group 0
-  // runs M(u) in half-phase 2u and V(u) in 2u+1; group 1 runs M(u) in 2u+1
-  // and V(u) in 2u+2.  K(u) and V(u-1) are read in M(u) only, so their
-  // buffers are free after half-phase 2u+1.
+  // measured).  Every half-phase ends in a barrier.  Wave group 0 runs M(u)
+  // in half-phase 2u and V(u) in 2u+1; group 1 (the loaders) runs V(u-1) in
+  // half-phase 2u, starting it with the loads of K(u+1) (buffer (u+1) % 2) and
+  // V(u) (buffer u % 2), and M(u) in 2u+1.  The barrier that ends half-phase
+  // 2u already waits for those loads (its release covers direct-to-LDS
+  // writes), so they land before the loaders' M(u) reads LDS; a bare barrier
+  // there, letting them land during M(u), measured 0-6 % slower, and a third
+  // buffer pair (loads a tile earlier) gained nothing.  K(u) and V(u-1) are
+  // read in M(u) only, so their buffers are free after half-phase 2u+1.
   const int n_compute = min(ntiles, w_last_tile + 1);  // tiles with work for this wave (uniform)
   const int grp1 = wave >= kPfWaves / 2;
   int ids_k[NBT], ids_v[NBT];
   fetch_ids(0, ids_v);
-  load_lds(0, ids_v, 0, false, s_k[0]);
+  load_lds(0, ids_v, 0, false, s_k[0], grp1);
   if (ntiles > 1) fetch_ids(1, ids_k);
   wait_lds_loads();
   __syncthreads();
@@ -567,8 +581,8 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   auto tile2 = [&](int u, auto ub, auto g) __attribute__((always_inline)) {
     constexpr int UB = decltype(ub)::value;
     constexpr int WG = decltype(g)::value;
-    if (u + 1 < ntiles) load_lds(u + 1, ids_k, 0, false, s_k[1 - UB]);
-    if (u < ntiles) load_lds(u, ids_v, kv_half, true, s_v[UB]);
+    if (u + 1 < ntiles) load_lds(u + 1, ids_k, 0, false, s_k[1 - UB], WG == 1);
+    if (u < ntiles) load_lds(u, ids_v, kv_half, true, s_v[UB], WG == 1);
     if constexpr (WG == 0) m_half(u, ub);
     else v_half(u - 1);
     __syncthreads();
@@ -577,7 +591,7 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     if (u + 2 < ntiles) fetch_ids(u + 2, ids_k);
     if (u + 1 < ntiles) fetch_ids(u + 1, ids_v);
     wait_lds_loads();
-    if (u < ntiles) zero_v_tail(s_v[UB], u);
+    if (WG == 1 && u < ntiles) zero_v_tail(s_v[UB], u);
     __syncthreads();
   };
   using b0 = std::integral_constant<int, 0>;
