@@ -182,22 +182,31 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
   // 1e-36 of uniform, and masked keys still get exactly zero.
   const uint32_t qsign = scale_log2 < 0.0f ? 0x80008000u : 0u;
   const float cs = scale_log2 == 0.0f ? 1.17549435e-38f : fabsf(scale_log2);
+  // Every lane loads (rows past the chunk read its last row, in bounds) and
+  // zeroes afterwards, so all the loads are in flight at once rather than
+  // each waited inside its own branch.
   int my_pos[kRG];
   bf16x8_t qb[kRG][C::KC];
+  u32x4_t qv[kRG][C::KC];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
     const int r = wave * 16 * kRG + 16 * rg + r16;
     const int t = row_token(r);
     my_pos[rg] = t < n ? ctx - n + t : -1;
+    const int tc = min(t, n - 1);
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+      qv[rg][kc] = *reinterpret_cast<const u32x4_t *>(
+          q + ((((int64_t)q0 + tc) * num_q_heads + hq0 + row_head(r)) * D + kc * 32 + 8 * grp) * 2);
+  }
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    const bool live = my_pos[rg] >= 0;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (t < n) {
-        const char *p = q + ((((int64_t)q0 + t) * num_q_heads + hq0 + row_head(r)) * D + kc * 32 + 8 * grp) * 2;
-        v = *reinterpret_cast<const u32x4_t *>(p);
-        v ^= qsign;
-      }
-      qb[rg][kc] = as_bf16x8(v);
+      const u32x4_t v = qv[rg][kc] ^ qsign;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      qb[rg][kc] = as_bf16x8(live ? v : z);
     }
   }
 
