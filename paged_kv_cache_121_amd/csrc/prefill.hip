@@ -592,13 +592,27 @@ prefill_kernel(const char *__restrict__ pool, int64_t num_blocks, int num_kv_hea
     constexpr int WG = decltype(g)::value;
     if (u + 1 < ntiles) load_lds(u + 1, ids_k, 0, false, s_k[1 - UB], WG == 1);
     if (u < ntiles) load_lds(u, ids_v, kv_half, true, s_v[UB], WG == 1);
-    if constexpr (WG == 0) m_half(u, ub);
-    else v_half(u - 1);
+    // The next tiles' block ids (scalar loads) are fetched at the head of the
+    // vector half, which has no LDS waits for them to hold up, so they have
+    // landed by the barrier that ends the tile (its release waits for every
+    // scalar load in flight).
+    auto next_ids = [&]() __attribute__((always_inline)) {
+      if (u + 2 < ntiles) fetch_ids(u + 2, ids_k);
+      if (u + 1 < ntiles) fetch_ids(u + 1, ids_v);
+    };
+    if constexpr (WG == 0) {
+      m_half(u, ub);
+    } else {
+      next_ids();
+      v_half(u - 1);
+    }
     __syncthreads();
-    if constexpr (WG == 0) v_half(u);
-    else m_half(u, ub);
-    if (u + 2 < ntiles) fetch_ids(u + 2, ids_k);
-    if (u + 1 < ntiles) fetch_ids(u + 1, ids_v);
+    if constexpr (WG == 0) {
+      next_ids();
+      v_half(u);
+    } else {
+      m_half(u, ub);
+    }
     wait_lds_loads();
     if (WG == 1 && u < ntiles) zero_v_tail(s_v[UB], u);
     __syncthreads();
