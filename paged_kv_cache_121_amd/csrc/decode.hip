@@ -59,8 +59,8 @@ namespace pa {
 namespace {
 
 // Partitions of kMidPartitionMin..kShortPartitionTokens tokens (mixed batches
-// of many pairs) take 8-wave workgroups and 8-token stages; groups of 8 take
-// 8-token stages up to kShortPartitionTokens.
+// of many pairs) take 8-wave workgroups and 8-token stages on the grid; groups
+// of 8 take 8-token stages up to kShortPartitionTokens.
 constexpr int kShortPartitionTokens = 2048;
 constexpr int kMidPartitionMin = 1024;
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup L is dispatched to XCD L % 8
@@ -967,8 +967,10 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   //   per wave; short contexts reach their first score sooner: up to 27 %
   //   faster on 128-token contexts, the same on long ones), except partitions
   //   of 1,024-2,048 tokens -- the many-pair mixed batches -- which take 8 waves
-  //   and 8-token stages (4-6 % faster there; 4 % slower on 4,096-token
-  //   partitions, 39 % slower on 256-token ones);
+  //   and 8-token stages on the grid (4-6 % faster there; 4 % slower on
+  //   4,096-token partitions, 39 % slower on 256-token ones); a work-list
+  //   launch keeps 4-wave workgroups, twice as many items in flight per
+  //   compute unit (0.9 % faster on 512 lognormal contexts);
   // - groups of 8 carry twice the arithmetic per token: bf16 pools with
   //   blocks of 16 or more take their scores from the matrix cores
   //   (16-token stages); otherwise 8-token stages up to 2,048-token
@@ -998,7 +1000,7 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
     kernel = pick(ch16{}, w4{}, std::true_type{});
   } else if constexpr (G > 4) {
     kernel = part_tokens <= kShortPartitionTokens ? pick(ch8{}, w4{}, vec{}) : pick(ch16{}, w4{}, vec{});
-  } else if (mid) {
+  } else if (mid && !listed) {
     kernel = pick(ch8{}, w8{}, vec{});
     waves = 8;
   }
