@@ -287,7 +287,9 @@ def read_ceiling(dev, total_bytes: int = 1 << 30, reps: int = 20, seed: int = 0)
     pieces of 4, 16 and 64 KiB (read_probe.hip: the decode kernel's 16-byte non-temporal loads,
     1 KiB per wavefront load), best over a sweep of grid sizes and loads in flight.  The decode
     of a paged cache reads 4 KiB (block, head) tiles of randomly placed blocks, so the random
-    4 KiB rate is its practical ceiling; HIP events over ``reps`` launches after a settle."""
+    4 KiB rate is its practical ceiling; HIP events over ``reps`` launches after a settle.
+    ``in_order_lds_dma``: the in-order read through direct-to-LDS loads (global_load_lds,
+    the prefill's load path), 2-8 chunks in flight per wave."""
     import ctypes
 
     import torch
@@ -328,6 +330,29 @@ def read_ceiling(dev, total_bytes: int = 1 << 30, reps: int = 20, seed: int = 0)
         out[label] = {"piece_bytes": piece, "best_gbs": round(rates[best], 1),
                       "pct_hbm_peak": round(100 * rates[best] / HBM_PEAK_GBS, 2), "best_launch": best,
                       "all_gbs": {k: round(v, 1) for k, v in rates.items()}}
+    # the same in-order read through direct-to-LDS loads (the prefill's path)
+    lib.pa_probe_read_lds.restype = ctypes.c_int
+    lib.pa_probe_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    rates = {}
+    for grid in (256, 512, 1024, 2048):
+        for u in (2, 4, 8):
+            def run_lds():
+                rc = lib.pa_probe_read_lds(ctypes.c_void_p(buf.data_ptr()), total_bytes, grid, u,
+                                           ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                assert rc == 0, rc
+            settle(run_lds, ms=20.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                run_lds()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rates[f"grid{grid}_x{u}"] = total_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    best = max(rates, key=rates.get)
+    out["in_order_lds_dma"] = {"piece_bytes": total_bytes, "best_gbs": round(rates[best], 1),
+                               "pct_hbm_peak": round(100 * rates[best] / HBM_PEAK_GBS, 2), "best_launch": best,
+                               "all_gbs": {k: round(v, 1) for k, v in rates.items()}}
     del buf, sink
     torch.cuda.empty_cache()
     return {"bytes": total_bytes, "reps": reps, **out}

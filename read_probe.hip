@@ -3,8 +3,9 @@
 // reads a buffer in pieces of a given size taken in a given order (in order,
 // or randomly placed like the physical blocks of a paged KV cache), with the
 // decode kernel's access style -- 16-byte non-temporal loads, one wavefront
-// load covering 1 KiB contiguous.  Built into libpa_probe.so, apart from the
-// library; nothing in the paged-attention path uses it.
+// load covering 1 KiB contiguous -- and, in order, with direct-to-LDS loads.
+// Built into libpa_probe.so, apart from the library; nothing in the
+// paged-attention path uses it.
 
 #include <hip/hip_runtime.h>
 
@@ -44,6 +45,33 @@ read_kernel(const char *__restrict__ base, const int32_t *__restrict__ order, in
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// The same in-order walk with direct-to-LDS loads (global_load_lds_dwordx4,
+// the prefill kernel's path): each wave moves its 1 KiB of a chunk into a
+// ring of kRing chunks in LDS and keeps U chunks' loads in flight (waits for
+// at most U - 1 outstanding after each issue).  Nothing reads the ring until
+// the end, when each thread sends one word of it to sink.
+constexpr int kRing = 8;
+
+template <int U>
+__global__ void __launch_bounds__(kThreads)
+read_lds_kernel(const char *__restrict__ base, int64_t num_chunks, uint32_t *__restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) char ring[kRing * kChunk];
+  const int64_t G = gridDim.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr unsigned kWait = (0x7u << 4) | (0xFu << 8) | ((U - 1) & 0xFu) | (((U - 1) >> 4) << 14);
+  int k = 0;
+  for (int64_t c = blockIdx.x; c < num_chunks; c += G, ++k) {
+    const char *src = base + c * kChunk + wave * 1024 + lane * 16;
+    char *dst = ring + (k % kRing) * kChunk + wave * 1024;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(kWait);  // vmcnt(U - 1)
+  }
+  __builtin_amdgcn_s_waitcnt((0x7u << 4) | (0xFu << 8));  // vmcnt(0)
+  __syncthreads();
+  sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = *reinterpret_cast<const uint32_t *>(&ring[threadIdx.x * 16]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +95,25 @@ int pa_probe_read(const void *base, int64_t piece_bytes, const int32_t *order, i
     case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, static_cast<const char *>(base), order, per_piece, chunks, sink); break;
     case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, static_cast<const char *>(base), order, per_piece, chunks, sink); break;
     case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, static_cast<const char *>(base), order, per_piece, chunks, sink); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Reads `bytes` (a multiple of 4 KiB) from `base` in order with direct-to-LDS
+// loads, `grid` workgroups of 256 threads, `unroll` (2, 4, 8 or 16) chunks in
+// flight per wave; `sink` (device, grid * 256 uint32) receives a value per
+// thread.  Enqueues one kernel on `stream`; returns 0, -1 for invalid
+// arguments (nothing launched), or -4 when the launch fails.
+int pa_probe_read_lds(const void *base, int64_t bytes, int grid, int unroll, uint32_t *sink, hipStream_t stream) {
+  if (base == nullptr || sink == nullptr || bytes <= 0 || bytes % kChunk != 0 || grid <= 0) return -1;
+  const int64_t chunks = bytes / kChunk;
+  const char *b = static_cast<const char *>(base);
+  switch (unroll) {
+    case 2: hipLaunchKernelGGL(read_lds_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, b, chunks, sink); break;
+    case 4: hipLaunchKernelGGL(read_lds_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, b, chunks, sink); break;
+    case 8: hipLaunchKernelGGL(read_lds_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, b, chunks, sink); break;
+    case 16: hipLaunchKernelGGL(read_lds_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, b, chunks, sink); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
